@@ -1,0 +1,192 @@
+"""Attention forward over dequantised operands, step by step.
+
+What is computed (the readings are stated where the pages leave a step open):
+
+1. Dequantise Q, K, V in fp64: value = code x scale of the token's 64-token
+   block (#2711 page, "코드 분석" 2: the block scales undo the quantisation
+   after BMM1 / BMM2), or the bf16 value itself for an unscaled operand.
+   Paged K/V (#4474 page, "코드 분석" 2 and the block-sparse paged-KV entry
+   point) are first gathered into logical token order through the page table.
+2. Scores in log2 units: s2 = (q . k) * softmax_scale * log2(e).
+3. Valid pairs: causal (bottom-right aligned), and the block mask at
+   Q64 x KV256 granularity (#4474 page, "코드 분석" 1: the Q64/KV256 tile is the
+   block-sparse unit).
+4. Online softmax with lazy correction (#5900 page, "코드 분석" 3, first
+   bullet: O is rescaled only when the row maximum has grown by 2^8): keys are
+   visited in ascending 64-key sub-tiles; a row's reference maximum m moves to
+   the sub-tile maximum t only when m is unset or t - m > 8 (log2 units), and
+   only then are the running numerator and denominator multiplied by 2^(m - t).
+   P = 2^(s2 - m) is therefore at most 2^8.
+5. P is quantised to the PV operand format before BMM2 (#5900 page title and
+   "코드 분석" 1: P is an 8-bit operand of the PV product when V is 8-bit), with
+   the optional static per-head P scale sfs_p (#2711 page, "코드 분석" 2 lists
+   a P scale-factor pointer): w = Qp(P / sp) * sp.
+6. num += sum_j w_j V_j and den += sum_j w_j (the denominator uses the same
+   quantised weights as the numerator).
+7. O = num / den; a row with no valid key gives 0.
+
+``mode="exact"`` replaces step 4 by the true row maximum (no rescaling);
+``p_format=None`` skips step 5.  Together they give plain softmax attention.
+"""
+import math
+
+import numpy as np
+
+from .codecs import bf16_round64, e4m3_decode, e4m3_round
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def dequantize(codes, fmt, scales=None, block_tokens=64):
+    """fp64 values of a [B, S, H, D] operand.
+
+    fmt: "int8" (int8 codes), "e4m3" (uint8 bit patterns) or "bf16" (float32
+    array holding bf16 values).  scales: float32 [B, H, ceil(S/64)] or None.
+    """
+    if fmt == "int8":
+        v = np.asarray(codes, dtype=np.int8).astype(np.float64)
+    elif fmt == "e4m3":
+        v = e4m3_decode(codes)
+    elif fmt == "bf16":
+        v = np.asarray(codes, dtype=np.float32).astype(np.float64)
+    else:
+        raise ValueError(fmt)
+    if scales is not None:
+        S = v.shape[1]
+        tok_blk = np.arange(S) // block_tokens                     # [S]
+        s = np.asarray(scales, dtype=np.float64)[:, :, tok_blk]     # [B, H, S]
+        v = v * np.transpose(s, (0, 2, 1))[..., None]
+    return v
+
+
+def gather_pages(pool, page_table, S, page_size=16):
+    """Logical [B, S, H, D] view of a paged pool [num_pages, page_size, H, D].
+
+    page_table[b, p] is the physical page holding logical tokens
+    [p*page_size, (p+1)*page_size) of sequence b.
+    """
+    pool = np.asarray(pool)
+    pt = np.asarray(page_table)
+    tok = np.arange(S)
+    phys = pt[:, tok // page_size]                 # [B, S]
+    return pool[phys, tok % page_size]             # [B, S, H, D]
+
+
+def _quantize_p(p, p_format):
+    if p_format is None:
+        return p
+    if p_format == "e4m3":
+        return e4m3_round(p)
+    if p_format == "bf16":
+        return bf16_round64(p)
+    raise ValueError(p_format)
+
+
+def valid_pairs(rows, Sq, Skv, causal, mask_rows):
+    """Boolean [len(rows), Skv]: which (query, key) pairs take part.
+
+    mask_rows: None or a boolean [len(rows), Skv] already expanded from the
+    block mask.  Causal alignment is bottom-right: key j is visible from
+    query i when j <= i + Skv - Sq.
+    """
+    j = np.arange(Skv)[None, :]
+    v = np.ones((len(rows), Skv), dtype=bool)
+    if causal:
+        v &= j <= (np.asarray(rows)[:, None] + Skv - Sq)
+    if mask_rows is not None:
+        v &= mask_rows
+    return v
+
+
+def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
+                   mask_rows=None, mode="lazy", p_format=None, sp=1.0,
+                   tau=8.0, sub_tile=64):
+    """One (batch, head): q [n, D] for query indices ``rows``; k, v [Skv, D].
+
+    Returns O [n, D] in fp64.
+    """
+    n, D = q.shape
+    Skv = k.shape[0]
+    valid = valid_pairs(rows, Sq, Skv, causal, mask_rows)
+    with np.errstate(invalid="ignore", over="ignore"):
+        s2 = (q @ k.T) * (softmax_scale * LOG2E)
+    if mode == "exact":
+        m = np.where(valid, s2, -np.inf).max(axis=1) if Skv else np.full(n, -np.inf)
+    else:
+        m = np.full(n, -np.inf)
+    num = np.zeros((n, D))
+    den = np.zeros(n)
+    for k0 in range(0, Skv, sub_tile):
+        cols = slice(k0, min(k0 + sub_tile, Skv))
+        vs = valid[:, cols]
+        if not vs.any():
+            continue
+        with np.errstate(invalid="ignore", over="ignore"):
+            s = np.where(vs, s2[:, cols], -np.inf)
+        if mode == "lazy":
+            t = s.max(axis=1)
+            has = vs.any(axis=1)
+            with np.errstate(invalid="ignore"):
+                trig = has & ((m == -np.inf) | (t - m > tau))
+                alpha = np.where(m == -np.inf, 0.0, np.exp2(np.where(trig, m - t, 0.0)))
+            num[trig] *= alpha[trig, None]
+            den[trig] *= alpha[trig]
+            m = np.where(trig, t, m)
+        with np.errstate(invalid="ignore", over="ignore"):
+            p = np.where(vs, np.exp2(s - m[:, None]), 0.0)
+        w = _quantize_p(p / sp, p_format) * sp
+        # keys valid for no row of this block are never read (they may hold
+        # anything, NaN included)
+        col_used = vs.any(axis=0)
+        vv = np.where(col_used[:, None], v[cols], 0.0)
+        num += w @ vv
+        den += w.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where(den[:, None] > 0, num / np.where(den > 0, den, 1.0)[:, None], 0.0)
+    return out
+
+
+def expand_block_mask(block_mask_bh, rows, Skv, mask_block_q=64, mask_block_kv=256):
+    """Boolean [len(rows), Skv] from one (batch, head) block mask [nqb, nkb]."""
+    bm = np.asarray(block_mask_bh) != 0
+    qb = np.asarray(rows) // mask_block_q
+    kb = np.arange(Skv) // mask_block_kv
+    return bm[qb][:, kb]
+
+
+def attention(qd, kd, vd, *, softmax_scale=None, causal=False, block_mask=None,
+              mode="lazy", p_format=None, sfs_p=None, tau=8.0, sub_tile=64,
+              rows=None, heads=None, mask_block_q=64, mask_block_kv=256):
+    """Attention over dequantised fp64 operands.
+
+    qd [B, Sq, Hq, D]; kd, vd [B, Skv, Hkv, D] in logical token order.  Query
+    head h reads key/value head h // (Hq // Hkv) (consecutive query heads
+    share a key/value head, the heads_q_per_kv grouping of the #4474 page,
+    "코드 분석" 1).  block_mask: None or [B, Hq, ceil(Sq/64), ceil(Skv/256)]
+    (non-zero = active).  rows: optional query indices to compute (rows are
+    independent); heads: optional list of (b, hq) pairs.
+
+    Returns fp64 [B, len(rows) or Sq, Hq, D]; entries of heads not computed
+    are NaN.
+    """
+    B, Sq, Hq, D = qd.shape
+    Skv, Hkv = kd.shape[1], kd.shape[2]
+    assert Hq % Hkv == 0
+    group = Hq // Hkv
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    out = np.full((B, len(rows), Hq, D), np.nan)
+    for b, hq in heads:
+        hk = hq // group
+        mrows = None
+        if block_mask is not None:
+            mrows = expand_block_mask(block_mask[b, hq], rows, Skv, mask_block_q, mask_block_kv)
+        sp = 1.0 if sfs_p is None else float(sfs_p[hq])
+        out[b, :, hq] = attention_head(
+            qd[b, rows, hq], kd[b, :, hk], vd[b, :, hk], rows, Sq=Sq,
+            softmax_scale=softmax_scale, causal=causal, mask_rows=mrows, mode=mode,
+            p_format=p_format, sp=sp, tau=tau, sub_tile=sub_tile)
+    return out

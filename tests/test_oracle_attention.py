@@ -1,0 +1,232 @@
+"""Pins for the attention oracle: a library routine for the unquantised case,
+hand-derived lazy-rescale examples, and invariants the mathematics fixes."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attention, dequantize, gather_pages
+from oracle.codecs import e4m3_decode
+from oracle.quantize import quantize_blocks
+
+
+def _sdpa(qd, kd, vd, causal=False, block_mask=None, scale=None):
+    """torch's CPU scaled_dot_product_attention in fp64 (heads expanded for GQA)."""
+    B, Sq, Hq, D = qd.shape
+    Skv, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    q = torch.from_numpy(qd).permute(0, 2, 1, 3)
+    k = torch.from_numpy(kd).permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    v = torch.from_numpy(vd).permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    mask = torch.ones(B, Hq, Sq, Skv, dtype=torch.bool)
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Skv)[None, :]
+        mask &= (j <= i + Skv - Sq)
+    if block_mask is not None:
+        bm = torch.from_numpy(block_mask != 0)
+        mask &= bm.repeat_interleave(64, 2)[:, :, :Sq].repeat_interleave(256, 3)[..., :Skv]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,causal", [
+    (1, 5, 7, 1, 1, 16, False), (2, 70, 70, 4, 2, 16, True), (1, 33, 150, 6, 3, 8, False),
+    (1, 150, 130, 2, 1, 8, True), (2, 64, 64, 2, 2, 32, True)])
+@pytest.mark.parametrize("mode", ["lazy", "exact"])
+def test_unquantized_matches_torch_sdpa(B, Sq, Skv, Hq, Hkv, D, causal, mode):
+    qd = _rand((B, Sq, Hq, D), 1, 2.0)
+    kd = _rand((B, Skv, Hkv, D), 2, 2.0)
+    vd = _rand((B, Skv, Hkv, D), 3)
+    got = attention(qd, kd, vd, causal=causal, mode=mode)
+    ref = _sdpa(qd, kd, vd, causal=causal, scale=1 / math.sqrt(D))
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_unquantized_block_mask_matches_torch_sdpa():
+    B, S, H, D = 1, 600, 2, 8
+    rng = np.random.default_rng(9)
+    qd, kd, vd = (rng.standard_normal((B, S, H, D)) for _ in range(3))
+    nqb, nkb = -(-S // 64), -(-S // 256)
+    bm = (rng.random((B, H, nqb, nkb)) < 0.5).astype(np.uint8)
+    for qb in range(nqb):
+        bm[:, :, qb, min(qb // 4, nkb - 1)] = 1  # every row keeps a block
+    got = attention(qd, kd, vd, block_mask=bm)
+    assert np.allclose(got, _sdpa(qd, kd, vd, block_mask=bm, scale=1 / math.sqrt(D)), rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_scale_is_applied():
+    qd, kd, vd = _rand((1, 9, 1, 4), 4), _rand((1, 11, 1, 4), 5), _rand((1, 11, 1, 4), 6)
+    got = attention(qd, kd, vd, softmax_scale=0.37)
+    assert np.allclose(got, _sdpa(qd, kd, vd, scale=0.37), rtol=1e-10, atol=1e-12)
+
+
+def _hand_inputs(kvals):
+    Skv = 66
+    k = np.full(Skv, -1000.0)
+    k[[0, 1, 64, 65]] = kvals
+    v = np.zeros(Skv)
+    v[[0, 1, 64, 65]] = [1.0, 10.0, 100.0, 1000.0]
+    qd = np.ones((1, 1, 1, 1))
+    return qd, k.reshape(1, Skv, 1, 1), v.reshape(1, Skv, 1, 1)
+
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_lazy_rescale_hand_examples(golden_dir, case):
+    g = json.load(open(os.path.join(golden_dir, "lazy_hand.json")))["cases"][case]
+    qd, kd, vd = _hand_inputs(g["k"])
+    run = lambda **kw: float(attention(qd, kd, vd, softmax_scale=math.log(2.0), **kw)[0, 0, 0, 0])
+    assert run(mode="lazy", p_format="e4m3") == pytest.approx(g["lazy_e4m3"], rel=1e-12)
+    assert run(mode="exact", p_format="e4m3") == pytest.approx(g["exact_e4m3"], rel=1e-12)
+    if "unquantized" in g:
+        assert run(mode="lazy") == pytest.approx(g["unquantized"], rel=1e-12)
+        assert run(mode="exact") == pytest.approx(g["unquantized"], rel=1e-12)
+    if "lazy_bf16" in g:
+        assert run(mode="lazy", p_format="bf16") == pytest.approx(g["lazy_bf16"], rel=1e-12)
+    if "lazy_e4m3_sp_quarter" in g:
+        assert run(mode="lazy", p_format="e4m3", sfs_p=[0.25]) == pytest.approx(g["lazy_e4m3_sp_quarter"], rel=1e-12)
+
+
+@pytest.mark.parametrize("tau", [0.0, 3.0, 8.0, 30.0])
+def test_lazy_equals_exact_without_p_quantisation(tau):
+    # large score range so that rescales happen for every tau
+    qd, kd, vd = _rand((1, 40, 2, 16), 11, 3.0), _rand((1, 300, 2, 16), 12, 3.0), _rand((1, 300, 2, 16), 13)
+    a = attention(qd, kd, vd, mode="lazy", tau=tau)
+    b = attention(qd, kd, vd, mode="exact")
+    assert np.allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_lazy_equals_exact_when_max_is_in_first_subtile():
+    rng = np.random.default_rng(14)
+    D, Skv = 16, 300
+    qd = rng.standard_normal((1, 50, 1, D))
+    kd = rng.standard_normal((1, Skv, 1, D))
+    vd = rng.standard_normal((1, Skv, 1, D))
+    qd[..., 0] = 1.0
+    kd[..., 0] = 0.0
+    kd[0, 0, 0, 0] = 200.0  # key 0 dominates every row
+    a = attention(qd, kd, vd, mode="lazy", p_format="e4m3")
+    b = attention(qd, kd, vd, mode="exact", p_format="e4m3")
+    assert np.array_equal(a, b)
+
+
+def _quantized_case(seed, B=1, Sq=130, Skv=200, Hq=2, Hkv=2, D=32, spread=2.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Sq, Hq, D)).astype(np.float32) * spread
+    k = rng.standard_normal((B, Skv, Hkv, D)).astype(np.float32) * spread
+    v = rng.standard_normal((B, Skv, Hkv, D)).astype(np.float32)
+    qc, qs = quantize_blocks(q, "e4m3")
+    kc, ks = quantize_blocks(k, "e4m3")
+    vc, vs = quantize_blocks(v, "e4m3")
+    return (dequantize(qc, "e4m3", qs), dequantize(kc, "e4m3", ks), dequantize(vc, "e4m3", vs))
+
+
+@pytest.mark.parametrize("mode", ["lazy", "exact"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(mode, causal):
+    qd, kd, vd = _quantized_case(15)
+    ones = np.ones_like(vd)
+    o = attention(qd, kd, ones, mode=mode, p_format="e4m3", causal=causal)
+    assert np.allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["lazy", "exact"])
+def test_constant_v_gives_v(mode):
+    qd, kd, vd = _quantized_case(16)
+    cv = np.broadcast_to(vd[:, :1], vd.shape).copy()  # every key carries key 0's value
+    o = attention(qd, kd, cv, mode=mode, p_format="e4m3")
+    assert np.allclose(o, np.repeat(cv[:, :1], qd.shape[2] // kd.shape[2], axis=2)[:, [0] * qd.shape[1]], rtol=1e-12, atol=1e-12)
+
+
+def test_key_permutation_invariance_unquantized():
+    qd, kd, vd = _rand((1, 20, 2, 8), 17), _rand((1, 90, 2, 8), 18), _rand((1, 90, 2, 8), 19)
+    perm = np.random.default_rng(20).permutation(90)
+    a = attention(qd, kd, vd, mode="lazy")
+    b = attention(qd, kd[:, perm], vd[:, perm], mode="lazy")
+    assert np.allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_block_permutation_invariance_quantized_exact():
+    qd, kd, vd = _quantized_case(21, Skv=256)
+    perm = np.concatenate([np.arange(64) + 64 * b for b in [2, 0, 3, 1]])
+    a = attention(qd, kd, vd, mode="exact", p_format="e4m3")
+    b = attention(qd, kd[:, perm], vd[:, perm], mode="exact", p_format="e4m3")
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_masked_blocks_contribute_nothing_even_if_nan():
+    B, S, H, D = 1, 600, 2, 16
+    qd, kd, vd = (_rand((B, S, H, D), s) for s in (22, 23, 24))
+    nqb, nkb = 10, 3
+    bm = np.ones((B, H, nqb, nkb), dtype=np.uint8)
+    bm[:, :, :, 1] = 0  # keys 256..511 inactive for every query block
+    a = attention(qd, kd, vd, block_mask=bm, mode="lazy", p_format="e4m3")
+    kd2, vd2 = kd.copy(), vd.copy()
+    kd2[:, 256:512] = np.nan
+    vd2[:, 256:512] = np.nan
+    b = attention(qd, kd2, vd2, block_mask=bm, mode="lazy", p_format="e4m3")
+    assert np.all(np.isfinite(b)) and np.array_equal(a, b)
+    ref = _sdpa(qd, kd, vd, block_mask=bm, scale=1 / math.sqrt(D))
+    assert np.allclose(attention(qd, kd2, vd2, block_mask=bm), ref, rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    qd, kd, vd = _quantized_case(25, Hq=6, Hkv=2)
+    a = attention(qd, kd, vd, mode="lazy", p_format="e4m3")
+    b = attention(qd, np.repeat(kd, 3, axis=2), np.repeat(vd, 3, axis=2), mode="lazy", p_format="e4m3")
+    assert np.array_equal(a, b)
+
+
+def test_causal_row0_and_single_key():
+    qd, kd, vd = _quantized_case(26, Sq=100, Skv=100)
+    o = attention(qd, kd, vd, causal=True, mode="lazy", p_format="e4m3")
+    assert np.array_equal(o[:, 0], vd[:, 0])
+    o1 = attention(qd, kd[:, :1], vd[:, :1], mode="lazy", p_format="e4m3")
+    assert np.array_equal(o1, np.broadcast_to(vd[:, :1], o1.shape))
+
+
+def test_row_without_valid_key_is_zero():
+    qd, kd, vd = _rand((1, 70, 1, 8), 27), _rand((1, 300, 1, 8), 28), _rand((1, 300, 1, 8), 29)
+    bm = np.ones((1, 1, 2, 2), dtype=np.uint8)
+    bm[0, 0, 1, :] = 0  # query block 1 (rows 64..69) sees nothing
+    o = attention(qd, kd, vd, block_mask=bm, mode="lazy", p_format="e4m3")
+    assert np.all(o[0, 64:] == 0) and np.all(np.abs(o[0, :64]).sum(-1) > 0)
+
+
+def test_rows_subset_matches_full():
+    qd, kd, vd = _quantized_case(30, Sq=200)
+    rows = np.array([0, 63, 64, 199])
+    full = attention(qd, kd, vd, mode="lazy", p_format="e4m3", causal=True)
+    part = attention(qd, kd, vd, mode="lazy", p_format="e4m3", causal=True, rows=rows)
+    assert np.array_equal(full[:, rows], part)
+
+
+def test_dequantize_uses_the_tokens_block_scale():
+    codes = np.zeros((1, 130, 1, 2), dtype=np.int8)
+    codes[0, :, 0, 0] = 1
+    scales = np.array([[[2.0, 3.0, 5.0]]], dtype=np.float32)
+    d = dequantize(codes, "int8", scales)
+    assert np.all(d[0, :64, 0, 0] == 2) and np.all(d[0, 64:128, 0, 0] == 3) and np.all(d[0, 128:, 0, 0] == 5)
+    assert np.all(d[..., 1] == 0)
+    e = dequantize(np.full((1, 1, 1, 1), 0x38, dtype=np.uint8), "e4m3", np.array([[[0.5]]], dtype=np.float32))
+    assert e.item() == 0.5
+
+
+def test_gather_pages():
+    rng = np.random.default_rng(31)
+    B, S, H, D, P = 2, 64, 1, 4, 16
+    logical = rng.standard_normal((B, S, H, D))
+    perm = rng.permutation(B * S // P)
+    pt = perm.reshape(B, S // P)
+    pool = np.zeros((B * S // P, P, H, D))
+    for b in range(B):
+        for p in range(S // P):
+            pool[pt[b, p]] = logical[b, p * P:(p + 1) * P]
+    assert np.array_equal(gather_pages(pool, pt, S, P), logical)
