@@ -1,0 +1,239 @@
+"""Throughput of the mixed-precision attention forward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already in
+HBM: block quantisation of the operands the workload quantises
+(fmha_quantize_blocks), then the fused attention forward (fmha_fwd).  The
+default workload is the DiT-scale self-attention with bf16 Q/K and E4M3 V/P
+(B=1, H=40, S=32760, d=128, non-causal, 2^8 lazy rescale).
+
+Prints one JSON line.  Timing: W untimed warm-up steps, then K steps between
+two device synchronisations; per-kernel durations come from HIP events
+recorded on the launch stream around every launch of the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--workload dit] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published dense peaks of MI355X (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "int8": 5000.0}
+HBM_PEAK_GBS = 8000.0
+METRIC = "fmha_fwd TFLOP/s (4·B·H·Sq·Skv·d, mask-aware) + % of MI355X dtype MFMA peak"
+
+
+def mixed_peak(qk_fmt, pv_fmt):
+    """Dense MFMA peak of a step whose FLOPs split evenly between the QK^T
+    product (qk_fmt) and the PV product (pv_fmt): time-weighted harmonic mean."""
+    return 1.0 / (0.5 / PEAK[qk_fmt] + 0.5 / PEAK[pv_fmt])
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("attention.hip", "device_common.h"):
+        h.update(open(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pair_count(spec, data):
+    if spec.masked:
+        bm = data["block_mask"].astype(bool)
+        S = spec.S
+        # active (query block, key block) pairs, clipped to the sequence
+        qlen = np.minimum(64, S - 64 * np.arange(bm.shape[2]))
+        klen = np.minimum(256, S - 256 * np.arange(bm.shape[3]))
+        return int((bm * qlen[None, None, :, None] * klen[None, None, None, :]).sum())
+    return spec.pairs()
+
+
+def cpu_baseline(spec, data, budget_s=12.0):
+    """The oracle (as it stands) on a bounded row sample of the workload."""
+    from oracle.attention import attention, dequantize
+    from oracle.quantize import quantize_blocks
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    h = 0
+    hk = h // (spec.Hq // spec.Hkv)
+    sub = lambda x, hh: x[:1, :, [hh]]
+
+    def operand(x, fmt, hh):
+        if fmt == "bf16":
+            return sub(x, hh).astype(np.float64)
+        c, s = quantize_blocks(sub(x, hh), fmt)
+        return dequantize(c, fmt, s)
+
+    t0 = time.perf_counter()
+    qd = operand(data["q"], spec.q_fmt, h)
+    kd = operand(data["k"], spec.k_fmt, hk)
+    vd = operand(data["v"], spec.v_fmt, hk)
+    t_prep = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows_done, pairs_done, t_att = 0, 0, 0.0
+    bm = data.get("block_mask")
+    bm = None if bm is None else bm[:1, [h]]
+    while t_att < budget_s and rows_done < spec.S:
+        rows = np.sort(rng.choice(spec.S, size=min(64, spec.S), replace=False))
+        t0 = time.perf_counter()
+        attention(qd, kd, vd, causal=spec.causal, block_mask=bm, mode="lazy",
+                  p_format=spec.v_fmt, rows=rows, heads=[(0, 0)])
+        t_att += time.perf_counter() - t0
+        rows_done += len(rows)
+        if spec.causal:
+            pairs_done += int(np.minimum(rows + 1, spec.S).sum())
+        elif bm is not None:
+            pairs_done += int(sum(bm[0, 0, r // 64].sum() * 256 for r in rows))
+        else:
+            pairs_done += len(rows) * spec.S
+    flops = 4.0 * spec.D * pairs_done
+    return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} random query rows of head 0 (batch 0), all {spec.S} keys each, lazy E4M3-P "
+                      f"oracle in fp64 numpy; operand dequantisation ({t_prep:.1f} s) not counted; "
+                      f"{t_att:.1f} s of CPU time",
+            "seconds": round(t_att, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the attention of each (batch, head) is independent, so a multi-GPU "
+              "run is N copies of this one with a head slice each; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fmha_fwd_amd as F
+    from fmha_fwd_amd import workloads as W
+
+    spec = W.SPECS[args.workload]
+    data = W.generate(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    F.lib_handle()
+    q = torch.from_numpy(data["q"]).to(torch.bfloat16).to(dev)
+    k = torch.from_numpy(data["k"]).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(data["v"]).to(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+
+    # Buffers written by the step (allocated once, outside the timed region).
+    def codes_like(x, fmt):
+        return torch.empty(x.shape, dtype=torch.int8 if fmt == "int8" else torch.float8_e4m3fn, device=dev)
+
+    def scales_like(x):
+        return torch.empty((x.shape[0], x.shape[2], (x.shape[1] + 63) // 64), dtype=torch.float32, device=dev)
+
+    quant = []  # (input, fmt, codes, scales)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        fmt = getattr(spec, name + "_fmt")
+        if fmt != "bf16":
+            quant.append((name, x, fmt, codes_like(x, fmt), scales_like(x)))
+    ops = {"q": q, "k": k, "v": v}
+    sfs = {}
+    for name, x, fmt, c, s in quant:
+        ops[name] = c
+        sfs["sfs_" + name] = s
+    fwd_kw = dict(causal=spec.causal)
+    if spec.masked:
+        fwd_kw["block_mask"] = torch.from_numpy(data["block_mask"]).to(dev)
+    if spec.paged:
+        # A paged cache is quantised when tokens are written to it, not by the
+        # attention step: quantise K/V once here and scatter the codes into the
+        # page pool; the timed step quantises the other operands only.
+        pt = torch.from_numpy(data["page_table"]).to(dev)
+        fwd_kw.update(page_table=pt, page_size=spec.page_size, seq_len_kv=spec.S)
+        per_seq, ps = pt.shape[1], spec.page_size
+        for name, x, fmt, c, s in [e for e in quant if e[0] in ("k", "v")]:
+            F.quantize_blocks(x, fmt, codes=c, scales=s)
+            pool = torch.empty((spec.B * per_seq, ps, spec.Hkv, spec.D), dtype=c.dtype, device=dev)
+            pool[pt.reshape(-1).long()] = c.reshape(spec.B * per_seq, ps, spec.Hkv, spec.D)
+            ops[name] = pool
+        quant = [e for e in quant if e[0] not in ("k", "v")]
+    out = torch.empty((spec.B, spec.S, spec.Hq, spec.D), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for name, x, fmt, c, s in quant:
+            F.quantize_blocks(x, fmt, codes=c, scales=s, stream=stream)
+        kk, vv = ops["k"], ops["v"]
+        if ev is not None:
+            ev[1].record(stream)
+        F.fwd(ops["q"], kk, vv, out=out, stream=stream, **sfs, **fwd_kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [e[0].elapsed_time(e[1]) for e in events]
+    f_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_step = wall * 1e3 / args.steps
+    fwd_ms = float(np.mean(f_ms))
+
+    pairs = pair_count(spec, data)
+    flops = 4.0 * spec.D * pairs
+    qk_fmt = "bf16" if spec.q_fmt == "bf16" or spec.k_fmt == "bf16" else spec.q_fmt
+    pv_fmt = spec.v_fmt
+    peak = mixed_peak(qk_fmt, pv_fmt)
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    quant_bytes = sum(x.numel() * 3 + s.numel() * 4 for _, x, _, _, s in quant)
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"fwd_{spec.name}_traffic.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    rec = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{qk_fmt}-qk/{pv_fmt}-pv",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "Sq": spec.S, "Skv": spec.S,
+                   "d": spec.D, "q": spec.q_fmt, "k": spec.k_fmt, "v": spec.v_fmt, "p": spec.v_fmt,
+                   "causal": spec.causal, "block_sparse": spec.masked, "paged": spec.paged,
+                   "unmasked_pairs": pairs, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "fmha_fwd", "frac_of_fp8_peak": achieved / PEAK["e4m3"]},
+        "fwd_ms": fwd_ms,
+        "quantize_ms": float(np.mean(q_ms)) if quant else 0.0,
+        "quantize_gbs": (quant_bytes / (np.mean(q_ms) * 1e-3) / 1e9) if quant else None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(spec, data)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

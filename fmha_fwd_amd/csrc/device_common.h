@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, number-format conversions and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+typedef __attribute__((ext_vector_type(2))) int v2i;
+typedef __attribute__((ext_vector_type(4))) int v4i;
+typedef __attribute__((ext_vector_type(8))) int v8i;
+typedef __attribute__((ext_vector_type(16))) int v16i;
+typedef __attribute__((ext_vector_type(2))) float v2f;
+typedef __attribute__((ext_vector_type(16))) float v16f;
+typedef __attribute__((ext_vector_type(8))) __bf16 v8bf;
+typedef __attribute__((ext_vector_type(4))) short v4s;
+typedef __attribute__((ext_vector_type(2))) unsigned short v2us;
+
+#define FMHA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// ---------------------------------------------------------------- MFMA
+// 32x32 output tiles.  Operand layout (checked on gfx950): lane l supplies row
+// (A) / column (B) l % 32 and the contraction slots of lane group l / 32;
+// result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+__device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+// E4M3 x E4M3 with unit block scales (E8M0 exponent 127 = 2^0).
+__device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------- formats
+// Two floats -> two E4M3 codes in byte pair `hi` of `old` (round to nearest
+// even; the hardware returns NaN instead of saturating at |x| >= 464, so
+// callers clamp first where that range can be reached).
+template <bool HI>
+__device__ __forceinline__ int pack_e4m3(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+template <bool HI>
+__device__ __forceinline__ v2f unpack_e4m3(int packed) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(packed, HI);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+}  // namespace fmha

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernels.
+// All strides here are in BYTES; every pointer is a device pointer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+enum Fmt : int { FMT_BF16 = 0, FMT_E4M3 = 1, FMT_INT8 = 2 };
+
+struct QuantArgs {
+  const uint8_t* x;
+  int64_t x_sb, x_ss, x_sh;
+  uint8_t* codes;
+  int64_t c_sb, c_ss, c_sh;
+  float* scales;
+  int B, S, H, nblk;
+  int out_fmt;  // FMT_INT8 or FMT_E4M3
+};
+
+hipError_t launch_quantize_blocks(const QuantArgs& a, hipStream_t stream);
+
+struct FwdArgs {
+  const uint8_t* q; int64_t q_sb, q_ss, q_sh;
+  const uint8_t* k; int64_t k_sb, k_ss, k_sh;   // paged: sb = page stride, ss = slot stride
+  const uint8_t* v; int64_t v_sb, v_ss, v_sh;
+  uint8_t* o; int64_t o_sb, o_ss, o_sh;
+  const float* sfs_q;   // [B, Hq, nblk_q] or null
+  const float* sfs_k;   // [B, Hkv, nblk_kv] or null
+  const float* sfs_v;   // [B, Hkv, nblk_kv] or null
+  int B, Sq, Skv, Hq, Hkv, group;
+  int nblk_q, nblk_kv;
+  float scale_log2;     // softmax_scale * log2(e)
+  float tau;
+  int causal;
+  const uint8_t* mask;  // null = dense
+  int64_t m_sb, m_sh, m_sqb;
+  int mask_kv_sub;      // 64-key sub-tiles per mask key block
+  const int32_t* page_table;  // null = contiguous
+  int64_t pt_sb;
+  int page_size, num_pages;
+  const float* sfs_p;   // [Hq] or null
+  int clamp_p;          // P / sp may reach the E4M3 overflow range
+};
+
+struct FwdKey {
+  int qf, kf, vf;
+  bool q_scaled, k_scaled, v_scaled;
+  bool masked, paged;
+};
+
+// Returns hipErrorInvalidValue (without launching) when no kernel instance
+// exists for the key; the caller validates that beforehand.
+bool fwd_supported(const FwdKey& key);
+hipError_t launch_fwd(const FwdKey& key, const FwdArgs& a, hipStream_t stream);
+
+}  // namespace fmha

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+Input generation only: no step of the attention method lives here, so the HIP
+path and the CPU oracle can both draw from it.  Every draw comes from numpy's
+PCG64 with ``SeedSequence(2711, spawn_key=(config index,))`` spawned into five
+child streams used in the order [Q, K, V, structure, mask]; normal draws are
+float32 rounded to bf16 (torch's round-to-nearest-even cast).
+
+Configurations (d = 128 throughout):
+  tiny    B=1 H=2  S=256    all bf16, unscaled, non-causal
+  dit_i8  B=1 H=24 S=4096   int8 Q/K + E4M3 V with 64-token block scales,
+                            2% outlier channels (3 per head) of Q and K x20
+  dit     B=1 H=40 S=32760  bf16 Q/K, E4M3 V with 64-token block scales
+  gqa     B=2 Hq=64 Hkv=8 S=8192, E4M3 Q/K/V with block scales, causal,
+                            per-head standard deviation ~ U(0.5, 2)
+  sparse  B=4 H=32 S=16384  bf16 Q, E4M3 K/V in 16-token pages (random page
+                            table), Q64 x KV256 block mask with 16 of 64 key
+                            blocks active per query block (diagonal always)
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED = 2711
+
+
+@dataclass(frozen=True)
+class Spec:
+    name: str
+    index: int
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    q_fmt: str          # "bf16" | "int8" | "e4m3"
+    k_fmt: str
+    v_fmt: str
+    causal: bool = False
+    masked: bool = False
+    paged: bool = False
+    page_size: int = 16
+    D: int = 128
+
+    @property
+    def q_scaled(self):
+        return self.q_fmt != "bf16"
+
+    @property
+    def k_scaled(self):
+        return self.k_fmt != "bf16"
+
+    @property
+    def v_scaled(self):
+        return self.v_fmt != "bf16"
+
+    def pairs(self):
+        """Unmasked (query, key) pairs: the FLOP count is 4 * D * pairs."""
+        per_head = self.S * self.S
+        if self.causal:
+            per_head = self.S * (self.S + 1) // 2
+        if self.masked:
+            per_head = None
+        if per_head is None:
+            return None
+        return self.B * self.Hq * per_head
+
+
+SPECS = {
+    "tiny": Spec("tiny", 0, 1, 2, 2, 256, "bf16", "bf16", "bf16"),
+    "dit_i8": Spec("dit_i8", 1, 1, 24, 24, 4096, "int8", "int8", "e4m3"),
+    "dit": Spec("dit", 2, 1, 40, 40, 32760, "bf16", "bf16", "e4m3"),
+    "gqa": Spec("gqa", 3, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True),
+    "sparse": Spec("sparse", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True, paged=True),
+}
+
+
+def streams(spec_index):
+    ss = np.random.SeedSequence(SEED, spawn_key=(spec_index,))
+    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5)]
+
+
+def to_bf16_values(x):
+    """float32 array -> float32 array of the nearest bf16 values (RNE)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def generate(spec):
+    """Host inputs of one configuration.
+
+    Returns a dict with q, k, v (float32 arrays holding bf16 values, shapes
+    [B, S, H, D], K/V in logical token order) and, where the configuration
+    has them, page_table (int32 [B, S/page]) and block_mask (uint8
+    [B, Hq, S/64, S/256]).
+    """
+    rq, rk, rv, rs, rm = streams(spec.index)
+    B, S, D = spec.B, spec.S, spec.D
+    q = _normal(rq, (B, S, spec.Hq, D))
+    k = _normal(rk, (B, S, spec.Hkv, D))
+    v = _normal(rv, (B, S, spec.Hkv, D))
+    out = {}
+    if spec.name.startswith("dit_i8"):
+        # 2% of the 128 channels (3 per head) of Q and of K carry x20 outliers
+        n_out = int(round(0.02 * D))
+        for x, H in ((q, spec.Hq), (k, spec.Hkv)):
+            for h in range(H):
+                ch = rs.choice(D, size=n_out, replace=False)
+                x[:, :, h, ch] *= np.float32(20.0)
+    if spec.name.startswith("gqa"):
+        sig_q = rs.uniform(0.5, 2.0, spec.Hq).astype(np.float32)
+        sig_k = rs.uniform(0.5, 2.0, spec.Hkv).astype(np.float32)
+        sig_v = rs.uniform(0.5, 2.0, spec.Hkv).astype(np.float32)
+        q *= sig_q[None, None, :, None]
+        k *= sig_k[None, None, :, None]
+        v *= sig_v[None, None, :, None]
+    if spec.paged:
+        per_seq = -(-S // spec.page_size)
+        perm = rs.permutation(B * per_seq).astype(np.int32)
+        out["page_table"] = perm.reshape(B, per_seq)
+    if spec.masked:
+        nqb, nkb = -(-S // 64), -(-S // 256)
+        active = max(1, nkb // 4)
+        mask = np.zeros((B, spec.Hq, nqb, nkb), dtype=np.uint8)
+        for b in range(B):
+            for h in range(spec.Hq):
+                for qb in range(nqb):
+                    diag = min(qb // 4, nkb - 1)
+                    others = np.delete(np.arange(nkb), diag)
+                    pick = rm.choice(others, size=active - 1, replace=False)
+                    mask[b, h, qb, diag] = 1
+                    mask[b, h, qb, pick] = 1
+        out["block_mask"] = mask
+    out["q"] = to_bf16_values(q)
+    out["k"] = to_bf16_values(k)
+    out["v"] = to_bf16_values(v)
+    return out
+
+
+def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
+    """A reduced-size variant of a configuration (same formats and options)."""
+    s = SPECS[base]
+    return Spec(s.name + f"_S{S}", s.index, B or s.B, Hq or s.Hq, Hkv or s.Hkv, S, s.q_fmt, s.k_fmt, s.v_fmt,
+                kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged), s.page_size)

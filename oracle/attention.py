@@ -27,12 +27,22 @@ What is computed (the readings are stated where the pages leave a step open):
 
 ``mode="exact"`` replaces step 4 by the true row maximum (no rescaling);
 ``p_format=None`` skips step 5.  Together they give plain softmax attention.
+
+Rounding sensitivity (``flip_eps``): the pages fix no precision for the
+scores.  A kernel that forms s2 and 2^(s2 - m) in binary32 can put a P value
+that lies on a rounding boundary of Qp on the other side of it, which moves
+that key's weight by one step of the P format.  With ``flip_eps`` the oracle
+also returns, per output element, the sum over keys whose P / sp lies within
+relative distance flip_eps of such a boundary of |one-step change in w_j| *
+(share of w_j left after later rescales) * |V_j - O| / den: to first order,
+the most the output can move through such ties.  The output itself does not
+depend on flip_eps.
 """
 import math
 
 import numpy as np
 
-from .codecs import bf16_round64, e4m3_decode, e4m3_round
+from .codecs import bf16_round64, e4m3_decode, e4m3_round, rounding_gap
 
 LOG2E = 1.0 / math.log(2.0)
 
@@ -100,10 +110,11 @@ def valid_pairs(rows, Sq, Skv, causal, mask_rows):
 
 def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
                    mask_rows=None, mode="lazy", p_format=None, sp=1.0,
-                   tau=8.0, sub_tile=64):
+                   tau=8.0, sub_tile=64, flip_eps=None):
     """One (batch, head): q [n, D] for query indices ``rows``; k, v [Skv, D].
 
-    Returns O [n, D] in fp64.
+    Returns O [n, D] in fp64, or (O, rounding-sensitivity bound [n, D]) when
+    flip_eps is given.
     """
     n, D = q.shape
     Skv = k.shape[0]
@@ -116,6 +127,7 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
         m = np.full(n, -np.inf)
     num = np.zeros((n, D))
     den = np.zeros(n)
+    ties = []  # (cols, weight step at the tie, row max at that time) per sub-tile
     for k0 in range(0, Skv, sub_tile):
         cols = slice(k0, min(k0 + sub_tile, Skv))
         vs = valid[:, cols]
@@ -141,9 +153,22 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
         vv = np.where(col_used[:, None], v[cols], 0.0)
         num += w @ vv
         den += w.sum(axis=1)
+        if flip_eps is not None:
+            gap = np.where(vs, rounding_gap(p / sp, p_format, flip_eps) * sp, 0.0)
+            if gap.any():
+                ties.append((cols, gap, m.copy(), vv))
     with np.errstate(invalid="ignore", divide="ignore"):
         out = np.where(den[:, None] > 0, num / np.where(den > 0, den, 1.0)[:, None], 0.0)
-    return out
+    if flip_eps is None:
+        return out
+    bound = np.zeros((n, D))
+    safe_den = np.where(den > 0, den, np.inf)
+    for cols, gap, m_then, vv in ties:
+        with np.errstate(invalid="ignore", over="ignore"):
+            share = np.where(np.isfinite(m_then), np.exp2(m_then - m), 0.0)   # later rescales
+        wgt = gap * (share / safe_den)[:, None]                              # [n, keys]
+        bound += np.einsum("nk,nkd->nd", wgt, np.abs(vv[None, :, :] - out[:, None, :]))
+    return out, bound
 
 
 def expand_block_mask(block_mask_bh, rows, Skv, mask_block_q=64, mask_block_kv=256):
@@ -156,7 +181,7 @@ def expand_block_mask(block_mask_bh, rows, Skv, mask_block_q=64, mask_block_kv=2
 
 def attention(qd, kd, vd, *, softmax_scale=None, causal=False, block_mask=None,
               mode="lazy", p_format=None, sfs_p=None, tau=8.0, sub_tile=64,
-              rows=None, heads=None, mask_block_q=64, mask_block_kv=256):
+              rows=None, heads=None, mask_block_q=64, mask_block_kv=256, flip_eps=None):
     """Attention over dequantised fp64 operands.
 
     qd [B, Sq, Hq, D]; kd, vd [B, Skv, Hkv, D] in logical token order.  Query
@@ -167,7 +192,8 @@ def attention(qd, kd, vd, *, softmax_scale=None, causal=False, block_mask=None,
     independent); heads: optional list of (b, hq) pairs.
 
     Returns fp64 [B, len(rows) or Sq, Hq, D]; entries of heads not computed
-    are NaN.
+    are NaN.  With flip_eps, returns (O, rounding-sensitivity bound) of the
+    same shape (see the module docstring).
     """
     B, Sq, Hq, D = qd.shape
     Skv, Hkv = kd.shape[1], kd.shape[2]
@@ -179,14 +205,19 @@ def attention(qd, kd, vd, *, softmax_scale=None, causal=False, block_mask=None,
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
     out = np.full((B, len(rows), Hq, D), np.nan)
+    bound = np.full((B, len(rows), Hq, D), np.nan) if flip_eps is not None else None
     for b, hq in heads:
         hk = hq // group
         mrows = None
         if block_mask is not None:
             mrows = expand_block_mask(block_mask[b, hq], rows, Skv, mask_block_q, mask_block_kv)
         sp = 1.0 if sfs_p is None else float(sfs_p[hq])
-        out[b, :, hq] = attention_head(
+        r = attention_head(
             qd[b, rows, hq], kd[b, :, hk], vd[b, :, hk], rows, Sq=Sq,
             softmax_scale=softmax_scale, causal=causal, mask_rows=mrows, mode=mode,
-            p_format=p_format, sp=sp, tau=tau, sub_tile=sub_tile)
-    return out
+            p_format=p_format, sp=sp, tau=tau, sub_tile=sub_tile, flip_eps=flip_eps)
+        if flip_eps is None:
+            out[b, :, hq] = r
+        else:
+            out[b, :, hq], bound[b, :, hq] = r
+    return out if flip_eps is None else (out, bound)

@@ -103,3 +103,29 @@ def bf16_round64(x):
     spacing_exp = np.where(a >= 2.0 ** -126, e - 8, -133)
     q = np.rint(np.ldexp(a, -spacing_exp))  # rint: half to even
     return np.copysign(np.ldexp(q, spacing_exp), x)
+
+
+def rounding_gap(x, p_format, eps):
+    """Where x is within relative distance eps of a rounding boundary of the
+    format (the midpoint of two neighbouring representable values), return
+    the distance between those two values; 0 elsewhere.
+
+    An implementation that computes x in lower precision than this oracle may
+    land on the other side of such a boundary; the result then moves by one
+    step of the format.  x >= 0 (softmax weights).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if p_format == "e4m3":
+        lo_i = np.clip(np.searchsorted(_POS, x, side="right") - 1, 0, len(_POS) - 2)
+        lo, hi = _POS[lo_i], _POS[lo_i + 1]
+    elif p_format == "bf16":
+        _, e = np.frexp(np.maximum(x, 2.0 ** -133))
+        step = np.ldexp(1.0, np.maximum(e - 8, -133))
+        lo = np.floor(x / step) * step
+        hi = lo + step
+    else:
+        return np.zeros_like(x)
+    mid = (lo + hi) / 2
+    near = np.abs(x - mid) <= eps * np.maximum(x, 2.0 ** -133)
+    near &= x < E4M3_MAX if p_format == "e4m3" else True
+    return np.where(near, hi - lo, 0.0)

@@ -15,3 +15,19 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+_WORKLOADS = {}
+
+
+@pytest.fixture(scope="session")
+def workload_cache():
+    """Seeded host inputs of the named full-size workload, generated once."""
+    from fmha_fwd_amd import workloads as W
+
+    def get(name):
+        if name not in _WORKLOADS:
+            _WORKLOADS.clear()  # keep one full-size workload in memory at a time
+            _WORKLOADS[name] = W.generate(W.SPECS[name])
+        return _WORKLOADS[name]
+    return get

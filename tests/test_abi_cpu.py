@@ -1,0 +1,149 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, agrees with the header on struct layout, and rejects bad arguments
+before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fmha_fwd_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.LIB_PATH):
+        pytest.skip("libfmha.so not built")
+    return F.lib_handle()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[a-z_0-9 \*]+?\b(fmha_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == set(F.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+    assert lib.fmha_abi_version() == 0x000100
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = [f for f, _ in F.FmhaFwdParams._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
+           'printf("%zu %zu\\n", sizeof(fmha_fwd_params), sizeof(fmha_tensor));']
+    src += [f'printf("%zu\\n", offsetof(fmha_fwd_params, {f}));' for f in fields]
+    src += [f'printf("%zu\\n", offsetof(fmha_tensor, {f}));' for f, _ in F.FmhaTensor._fields_]
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", str(c), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(F.FmhaFwdParams) and vals[1] == ctypes.sizeof(F.FmhaTensor)
+    offs = vals[2:2 + len(fields)]
+    assert offs == [getattr(F.FmhaFwdParams, f).offset for f in fields]
+    toffs = vals[2 + len(fields):]
+    assert toffs == [getattr(F.FmhaTensor, f).offset for f, _ in F.FmhaTensor._fields_]
+
+
+FAKE = 0x10000  # a 16-byte aligned address that validation never dereferences
+
+
+def _tensor(dtype, sb=128 * 64 * 4, ss=128 * 4, sh=128, ptr=FAKE):
+    return F.FmhaTensor(ptr, dtype, sb, ss, sh)
+
+
+def _params(**kw):
+    p = F.FmhaFwdParams()
+    p.struct_size = ctypes.sizeof(F.FmhaFwdParams)
+    p.B, p.Sq, p.Skv, p.Hq, p.Hkv, p.D = 1, 64, 64, 4, 4, 128
+    p.q = _tensor(F.FMHA_DT_BF16)
+    p.k = _tensor(F.FMHA_DT_BF16)
+    p.v = _tensor(F.FMHA_DT_E4M3)
+    p.o = _tensor(F.FMHA_DT_BF16)
+    p.sfs_v = FAKE
+    p.sage_block_v = 64
+    p.lazy_rescale_log2 = 8.0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _call(lib, p):
+    return lib.fmha_fwd(ctypes.byref(p), None), lib.fmha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=64), F.FMHA_ERR_UNSUPPORTED, "D=64"),
+    (dict(Hq=6, Hkv=4), F.FMHA_ERR_INVALID, "multiple"),
+    (dict(Hkv=0), F.FMHA_ERR_INVALID, "Hkv"),
+    (dict(Sq=-1), F.FMHA_ERR_INVALID, "negative"),
+    (dict(struct_size=8), F.FMHA_ERR_INVALID, "struct_size"),
+    (dict(q=_tensor(F.FMHA_DT_BF16, ptr=FAKE + 8)), F.FMHA_ERR_INVALID, "aligned"),
+    (dict(q=_tensor(F.FMHA_DT_BF16, ptr=0)), F.FMHA_ERR_INVALID, "null"),
+    (dict(k=_tensor(F.FMHA_DT_BF16, ss=100)), F.FMHA_ERR_INVALID, "stride_s"),
+    (dict(o=_tensor(F.FMHA_DT_E4M3)), F.FMHA_ERR_UNSUPPORTED, "bf16"),
+    (dict(v=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "int8 V"),
+    (dict(q=_tensor(7)), F.FMHA_ERR_INVALID, "dtype"),
+    (dict(sage_block_v=32), F.FMHA_ERR_UNSUPPORTED, "sage_block_v"),
+    (dict(sage_block_v=0), F.FMHA_ERR_INVALID, "sfs_v given"),
+    (dict(q=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(k=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(lazy_rescale_log2=-1.0), F.FMHA_ERR_INVALID, "lazy"),
+    (dict(lazy_rescale_log2=float("nan")), F.FMHA_ERR_INVALID, "lazy"),
+    (dict(softmax_scale=float("inf")), F.FMHA_ERR_INVALID, "softmax_scale"),
+    (dict(causal=2), F.FMHA_ERR_INVALID, "causal"),
+    (dict(block_mask=FAKE, mask_block_q=128, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "mask_block_q"),
+    (dict(block_mask=FAKE, mask_block_q=64, mask_block_kv=100), F.FMHA_ERR_UNSUPPORTED, "mask_block_kv"),
+    (dict(page_table=FAKE, page_size=12, num_pages=4), F.FMHA_ERR_UNSUPPORTED, "page_size"),
+    (dict(page_table=FAKE, page_size=16, num_pages=0), F.FMHA_ERR_INVALID, "num_pages"),
+    (dict(sfs_p=FAKE + 2), F.FMHA_ERR_INVALID, "sfs_p"),
+])
+def test_fwd_rejects_bad_arguments_before_any_hip_call(lib, kw, code, msg):
+    rc, err = _call(lib, _params(**kw))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_fwd_null_params(lib):
+    assert lib.fmha_fwd(None, None) == F.FMHA_ERR_INVALID
+
+
+def test_fwd_empty_problem_is_a_no_op(lib):
+    rc, err = _call(lib, _params(Sq=0))
+    assert rc == F.FMHA_OK and err == ""
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=64), F.FMHA_ERR_UNSUPPORTED, "D=64"),
+    (dict(block=32), F.FMHA_ERR_UNSUPPORTED, "block_tokens"),
+    (dict(xdt=F.FMHA_DT_E4M3), F.FMHA_ERR_INVALID, "bf16"),
+    (dict(cdt=F.FMHA_DT_BF16), F.FMHA_ERR_INVALID, "int8 or e4m3"),
+    (dict(S=-3), F.FMHA_ERR_INVALID, "negative"),
+    (dict(xptr=FAKE + 4), F.FMHA_ERR_INVALID, "aligned"),
+    (dict(scales=0), F.FMHA_ERR_INVALID, "scales"),
+])
+def test_quantize_rejects_bad_arguments(lib, kw, code, msg):
+    x = _tensor(kw.get("xdt", F.FMHA_DT_BF16), ptr=kw.get("xptr", FAKE))
+    c = _tensor(kw.get("cdt", F.FMHA_DT_E4M3))
+    rc = lib.fmha_quantize_blocks(ctypes.byref(x), ctypes.byref(c), kw.get("scales", FAKE), 1, kw.get("S", 64), 4,
+                                  kw.get("D", 128), kw.get("block", 64), None)
+    err = lib.fmha_last_error().decode()
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_quantize_empty_is_a_no_op(lib):
+    x, c = _tensor(F.FMHA_DT_BF16), _tensor(F.FMHA_DT_INT8)
+    assert lib.fmha_quantize_blocks(ctypes.byref(x), ctypes.byref(c), None, 0, 64, 4, 128, 64, None) == F.FMHA_OK

@@ -1,0 +1,163 @@
+"""fmha_fwd on the GPU against the oracle on the same seeded inputs.
+
+Small shapes (full outputs, several tiles plus ragged tails) for every
+supported format combination and option, then the full-size workloads on
+sampled rows in the launch configuration the benchmark times.  Bar: max-abs
+error <= 1.5e-2 against the bf16-rounded quantisation-emulating oracle (one
+bf16 ulp differences counted apart), cosine >= 0.999 against it and >= 0.99
+against unquantised fp64 attention."""
+import numpy as np
+import pytest
+
+from fmha_fwd_amd import workloads as W
+import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _run_small(spec, **kw):
+    print(f"fwd small {spec}", flush=True)
+    data = W.generate(spec)
+    gpu, _ = Hn.gpu_run(spec, data, **kw)
+    ops = Hn.oracle_operands(spec, data)
+    okw = {}
+    if "sfs_p" in kw:
+        okw["sfs_p"] = kw["sfs_p"].cpu().numpy()
+    if "lazy_rescale_log2" in kw:
+        okw["tau"] = kw["lazy_rescale_log2"]
+    ref = Hn.oracle_output(spec, data, ops, **okw)
+    unq = Hn.unquantized_output(spec, data)
+    return Hn.assert_parity(gpu, ref, unq, what=spec.name)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 255, 320])
+@pytest.mark.parametrize("base", ["tiny", "dit_i8", "dit", "gqa"])
+def test_small_dense(base, S):
+    B, Hq, Hkv = {"tiny": (1, 2, 2), "dit_i8": (1, 3, 3), "dit": (2, 2, 2), "gqa": (2, 8, 2)}[base]
+    _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv))
+
+
+@pytest.mark.parametrize("S", [1, 65, 200, 320])
+@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8"])
+def test_small_causal(base, S):
+    _run_small(W.small_spec(base, S, B=1, Hq=4, Hkv=2, causal=True))
+
+
+@pytest.mark.parametrize("S", [64, 300, 768])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_sparse_paged(S, causal):
+    _run_small(W.small_spec("sparse", S, B=2, Hq=4, Hkv=2, causal=causal))
+
+
+@pytest.mark.parametrize("S", [256, 640])
+def test_small_sparse_contiguous(S):
+    _run_small(W.small_spec("sparse", S, B=1, Hq=2, Hkv=2, paged=False))
+
+
+def test_small_paged_dense():
+    _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=1, masked=False))
+
+
+def test_sfs_p_and_tau_variants():
+    spec = W.small_spec("gqa", 320, B=1, Hq=4, Hkv=2)
+    sp = torch.tensor([1.0, 0.25, 0.1, 2.0], dtype=torch.float32, device="cuda")
+    _run_small(spec, sfs_p=sp)
+    _run_small(spec, lazy_rescale_log2=0.0)
+    _run_small(spec, lazy_rescale_log2=12.0)
+
+
+def test_masked_blocks_with_nan_are_never_read():
+    import fmha_fwd_amd as F
+    spec = W.small_spec("sparse", 768, B=1, Hq=2, Hkv=2, paged=False)
+    data = W.generate(spec)
+    bm = data["block_mask"].copy()
+    bm[:, :, :, 1] = 0                      # keys 256..511 inactive for every query block
+    for qb in range(bm.shape[2]):
+        if not bm[0, 0, qb].any() or not bm[0, 1, qb].any():
+            bm[:, :, qb, 0] = 1
+    data["block_mask"] = bm
+    ref_gpu, t = Hn.gpu_run(spec, data)
+    k, v = t["k"].clone(), t["v"].clone()
+    k.view(torch.uint8)[:, 256:512] = 0x7F  # E4M3 NaN
+    v.view(torch.uint8)[:, 256:512] = 0x7F
+    o = F.fwd(t["q"], k, v, sfs_k=t["sfs_k"], sfs_v=t["sfs_v"], block_mask=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(got, ref_gpu)
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(got, Hn.oracle_output(spec, data, ops), what="masked-nan")
+
+
+def test_strided_q_and_output():
+    import fmha_fwd_amd as F
+    spec = W.small_spec("dit", 200, B=1, Hq=2, Hkv=2)
+    data = W.generate(spec)
+    qkv = torch.zeros((1, 200, 3, 2, 128), dtype=torch.bfloat16, device="cuda")
+    qkv[:, :, 0] = Hn.to_gpu_bf16(data["q"])
+    qkv[:, :, 1] = Hn.to_gpu_bf16(data["k"])
+    v, sv = F.quantize_blocks(Hn.to_gpu_bf16(data["v"]), "e4m3")
+    out = torch.zeros((1, 200, 4, 128), dtype=torch.bfloat16, device="cuda")
+    F.fwd(qkv[:, :, 0], qkv[:, :, 1], v, sfs_v=sv, out=out[:, :, 1:3])
+    torch.cuda.synchronize()
+    got = out[:, :, 1:3].float().cpu().numpy()
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(got, Hn.oracle_output(spec, data, ops), what="strided")
+    assert torch.count_nonzero(out[:, :, 0]) == 0 and torch.count_nonzero(out[:, :, 3]) == 0
+
+
+def test_no_valid_key_rows_are_zero():
+    import fmha_fwd_amd as F
+    spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)
+    data = W.generate(spec)
+    data["block_mask"][:, :, 2, :] = 0  # query block 2 sees nothing
+    gpu, _ = Hn.gpu_run(spec, data)
+    assert np.all(gpu[0, 128:192] == 0) and np.all(np.abs(gpu[0, :128]).sum(-1) > 0)
+
+
+def test_deterministic():
+    spec = W.small_spec("gqa", 700, B=1, Hq=8, Hkv=2, causal=True)
+    data = W.generate(spec)
+    a, _ = Hn.gpu_run(spec, data)
+    b, _ = Hn.gpu_run(spec, data)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = [
+    # name, heads (b, hq) checked, rows sampled
+    ("tiny", None, None),
+    ("dit_i8", [(0, 0), (0, 11), (0, 23)], "sample"),
+    ("dit", [(0, 0), (0, 39)], "sample"),
+    ("gqa", [(0, 0), (0, 7), (1, 63)], "sample"),
+    ("sparse", [(0, 0), (3, 31)], "sample"),
+]
+
+
+def _sample_rows(S, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(S, size=min(n, S), replace=False).tolist())
+    rows.update([0, 1, 63, 64, S - 1, S - 2, max(S - 57, 0)])
+    return np.array(sorted(r for r in rows if 0 <= r < S))
+
+
+@pytest.mark.parametrize("name,heads,rows", FULL)
+def test_full_workload_sampled_rows(name, heads, rows, workload_cache):
+    spec = W.SPECS[name]
+    print(f"fwd full {name}", flush=True)
+    data = workload_cache(name)
+    gpu, _ = Hn.gpu_run(spec, data)
+    r = None if rows is None else _sample_rows(spec.S)
+    hq_list = None if heads is None else sorted({h for _, h in heads})
+    hk_list = None if heads is None else sorted({h // (spec.Hq // spec.Hkv) for h in hq_list})
+    ops = Hn.oracle_operands(spec, data, heads_q=hq_list, heads_kv=hk_list)
+    ref = Hn.oracle_output(spec, data, ops, rows=r, heads=heads)
+    unq = Hn.unquantized_output(spec, data, rows=r, heads=heads)
+    g = gpu if r is None else gpu[:, r]
+    if heads is None:
+        Hn.assert_parity(g, ref, unq, what=name)
+    else:
+        for b, h in heads:
+            Hn.assert_parity(g[b, :, h], (ref[0][b, :, h], ref[1][b, :, h]), unq[b, :, h], what=f"{name} b={b} h={h}")

@@ -1,0 +1,94 @@
+"""fmha_quantize_blocks on the GPU against the oracle: bit-exact codes and
+scales (random, ragged tail, zero / tiny blocks, outliers, strided views, and
+the full-size workloads)."""
+import numpy as np
+import pytest
+
+from fmha_fwd_amd import workloads as W
+from oracle.quantize import quantize_blocks as oracle_quantize
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gpu_quant(x_np, fmt, view=None):
+    import fmha_fwd_amd as F
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(torch.bfloat16).cuda()
+    if view is not None:
+        x = view(x)
+    codes, scales = F.quantize_blocks(x, fmt)
+    torch.cuda.synchronize()
+    c = codes.view(torch.int8 if fmt == "int8" else torch.uint8).cpu().numpy()
+    return x, c, scales.cpu().numpy()
+
+
+def _bf16(x):
+    return W.to_bf16_values(x)
+
+
+def _check(x_vals, fmt, c, s):
+    rc, rs = oracle_quantize(x_vals, fmt)
+    assert np.array_equal(rs.view(np.uint32), s.view(np.uint32)), "scales differ"
+    bad = np.nonzero(rc != c)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {tuple(i[0] for i in bad)}"
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+@pytest.mark.parametrize("shape", [(1, 130, 3, 128), (2, 64, 2, 128), (1, 1, 1, 128), (1, 32760, 1, 128), (3, 257, 5, 128)])
+def test_random_blocks_bit_exact(fmt, shape):
+    print(f"quantize {fmt} {shape}", flush=True)
+    rng = np.random.default_rng(hash(shape) % 2 ** 32)
+    x = rng.standard_normal(shape).astype(np.float32)
+    x *= np.exp(rng.uniform(-6, 6, (shape[0], 1, shape[2], 1))).astype(np.float32)
+    x = _bf16(x)
+    _, c, s = _gpu_quant(x, fmt)
+    _check(x, fmt, c, s)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+def test_zero_tiny_and_outlier_blocks(fmt):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 320, 2, 128)).astype(np.float32)
+    x[0, 0:64] = 0.0                       # all-zero block
+    x[0, 64:128] = np.float32(2.0 ** -130)   # below 2^-126: scale 1, codes 0
+    x[0, 128:192, 0, 5] *= 1000.0          # outlier channel
+    x[0, 192:256] *= np.float32(2.0 ** -120)   # small but normal scales
+    x[0, 256:320] *= np.float32(2.0 ** 100)
+    x = _bf16(x)
+    _, c, s = _gpu_quant(x, fmt)
+    _check(x, fmt, c, s)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+def test_strided_views(fmt):
+    import fmha_fwd_amd as F
+    rng = np.random.default_rng(6)
+    big = _bf16(rng.standard_normal((2, 100, 6, 128)).astype(np.float32))
+    xg = torch.from_numpy(big).to(torch.bfloat16).cuda()[:, :, 1:4]          # head-strided view
+    out = torch.zeros((2, 100, 8, 128), dtype=torch.int8 if fmt == "int8" else torch.float8_e4m3fn, device="cuda")
+    codes_view = out[:, :, 2:5]
+    F.quantize_blocks(xg, fmt, codes=codes_view)
+    _, scales = F.quantize_blocks(xg, fmt)
+    torch.cuda.synchronize()
+    c = codes_view.contiguous().view(torch.int8 if fmt == "int8" else torch.uint8).cpu().numpy()
+    _check(big[:, :, 1:4], fmt, c, scales.cpu().numpy())
+    assert torch.count_nonzero(out[:, :, :2].view(torch.uint8)) == 0
+
+
+@pytest.mark.parametrize("name,which,heads", [
+    ("dit_i8", "q", None), ("dit_i8", "k", None), ("dit_i8", "v", None),
+    ("dit", "v", [0, 17, 39]),
+    ("gqa", "q", [0, 63]), ("gqa", "k", None), ("gqa", "v", [3]),
+    ("sparse", "k", [0, 31]), ("sparse", "v", [5]),
+])
+def test_full_workloads_bit_exact(name, which, heads, workload_cache):
+    spec = W.SPECS[name]
+    print(f"quantize full {name}.{which} heads={heads}", flush=True)
+    data = workload_cache(name)
+    fmt = getattr(spec, which + "_fmt")
+    x = data[which]
+    _, c, s = _gpu_quant(x, fmt)
+    if heads is not None:
+        x, c, s = x[:, :, heads], c[:, :, heads], s[:, heads]
+    _check(x, fmt, c, s)

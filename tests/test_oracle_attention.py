@@ -230,3 +230,31 @@ def test_gather_pages():
         for p in range(S // P):
             pool[pt[b, p]] = logical[b, p * P:(p + 1) * P]
     assert np.array_equal(gather_pages(pool, pt, S, P), logical)
+
+
+def test_rounding_sensitivity_bound_hand_example():
+    # EXACT mode, trigger case: P(key 0) = 2^-10 lies exactly on the E4M3
+    # boundary between 0 and 2^-9 (the tie goes to 0, O = 400).  Bound:
+    # 2^-9 * |v0 - O| / den = 2^-9 * 399 / 1.5.
+    qd, kd, vd = _hand_inputs([0.0, -1.0, 10.0, 9.0])
+    o, bound = attention(qd, kd, vd, softmax_scale=math.log(2.0), mode="exact", p_format="e4m3", flip_eps=1e-6)
+    assert o.item() == pytest.approx(400.0, rel=1e-12)
+    assert bound.item() == pytest.approx(2.0 ** -9 * 399 / 1.5, rel=1e-9)
+    # nudging key 0 over the boundary moves O by just under the bound
+    qd2, kd2, vd2 = _hand_inputs([1e-6, -1.0, 10.0, 9.0])
+    o2 = attention(qd2, kd2, vd2, softmax_scale=math.log(2.0), mode="exact", p_format="e4m3")
+    assert 0.5 < abs(o2.item() - o.item()) <= bound.item()
+    # no tie: zero bound, and the output does not depend on flip_eps
+    o3, b3 = attention(qd, kd, vd, softmax_scale=math.log(2.0), mode="lazy", p_format="e4m3", flip_eps=1e-6)
+    assert b3.item() == 0.0 and o3.item() == pytest.approx(399.61365853658536, rel=1e-12)
+
+
+@pytest.mark.parametrize("p_format", ["e4m3", "bf16"])
+def test_rounding_sensitivity_bound_covers_tiny_score_perturbations(p_format):
+    qd, kd, vd = _quantized_case(32, Sq=192, Skv=700, Hq=2, Hkv=1, spread=3.0)
+    o, bound = attention(qd, kd, vd, mode="lazy", p_format=p_format, flip_eps=1e-6)
+    for f in (1 + 2.0 ** -30, 1 - 2.0 ** -30):
+        o2 = attention(qd * f, kd, vd, mode="lazy", p_format=p_format)
+        # flips are bounded by `bound`; the rescale factors move continuously
+        # (relative 2^-30 of the scores, ~1e-8 here)
+        assert np.all(np.abs(o2 - o) <= bound + 1e-6)
