@@ -31,6 +31,8 @@
 //    before it is added to O (scales applied after BMM2).
 //  * sfs_p cancels between numerator and denominator, so it enters only the
 //    quantisation of P (exp2 argument shifted by log2 sfs_p).
+#include <type_traits>
+
 #include "device_common.h"
 #include "fmha_internal.h"
 
@@ -38,6 +40,10 @@ namespace fmha {
 namespace {
 
 constexpr int kSub = 64;  // keys per sub-tile: lazy-decision and V-scale unit
+#ifndef FMHA_DENSE_WAVES
+#define FMHA_DENSE_WAVES 8
+#endif
+constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per dense workgroup
 constexpr float kInf = __builtin_huge_valf();
 
 // Key held by row m of a 32-key MFMA tile: lane group g of the S^T result
@@ -45,34 +51,32 @@ constexpr float kInf = __builtin_huge_valf();
 __device__ __forceinline__ int sigma(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
-// XOR swizzles of 16-byte chunks inside an LDS row (row index = key in tile),
-// chosen so that the 16 rows one MFMA-operand read touches at a time, and the
-// 8 consecutive rows of a transposing read, fall in distinct banks.
-__device__ __forceinline__ int swz256(int key) { return (key & 7) | ((key & 16) >> 1); }
-__device__ __forceinline__ int swz128(int key) { return ((key >> 1) & 3) | ((key >> 2) & 4); }
-
-template <int KROW>
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * KROW + ((chunk ^ (KROW == 256 ? swz256(row) : swz128(row))) << 4);
-}
 
 template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_>
 struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
   static constexpr int MT = QF;                                  // QK operand format
-  static constexpr int KROW = MT == FMT_BF16 ? 256 : 128;        // LDS bytes per K row
+  static constexpr int KROW = MT == FMT_BF16 ? 256 : 128;        // bytes per K row (LDS format)
   static constexpr int VROW = VF == FMT_BF16 ? 256 : 128;
-  static constexpr int KGROW = KF == FMT_BF16 ? 256 : 128;       // HBM bytes per K row
-  static constexpr int K_TILE = kSub * KROW;
-  static constexpr int V_TILE = kSub * VROW;
-  static constexpr int STAGE = K_TILE + V_TILE;
+  static constexpr int KGROW = KF == FMT_BF16 ? 256 : 128;       // bytes per K row in HBM
+  // LDS rows are padded by one 16-byte chunk: consecutive rows start one
+  // chunk apart in the 64 x 4-byte banks, so the 16 rows an MFMA operand read
+  // touches at a time, and the 8 rows of a transposing read, hit distinct banks
+  // while every lane reads at a fixed offset from its own base address.
+  static constexpr int KP = KROW + 16, VP = VROW + 16;
+  static constexpr int K_BUF = kSub * KP, V_BUF = kSub * VP;
+  static constexpr int LDS_BYTES = 2 * (K_BUF + V_BUF);
+  static constexpr bool K_DMA = KROW == KGROW;                   // HBM -> LDS without conversion
   static constexpr int NT = NW * 64;
-  static constexpr int K_CPR = KGROW / 16;                       // 16-byte chunks per row
-  static constexpr int V_CPR = VROW / 16;
-  static constexpr int K_LOADS = kSub * K_CPR / NT;
-  static constexpr int V_LOADS = kSub * V_CPR / NT;
-  static_assert(kSub * K_CPR % NT == 0 && kSub * V_CPR % NT == 0, "tile / thread mismatch");
+  static constexpr int K_CPR = KROW / 16, KP_CPR = KP / 16;      // 16-byte chunks per row
+  static constexpr int V_CPR = VROW / 16, VP_CPR = VP / 16;
+  static constexpr int K_DMA_OPS = K_BUF / 1024;                 // 1 KB per wave-wide DMA
+  static constexpr int V_DMA_OPS = V_BUF / 1024;
+  static_assert(K_BUF % 1024 == 0 && V_BUF % 1024 == 0, "DMA granularity");
+  static constexpr int KG_CPR = KGROW / 16;                      // register path (widening K)
+  static constexpr int K_REG_LOADS = K_DMA ? 0 : kSub * KG_CPR / NT;
+  static_assert(K_DMA || kSub * KG_CPR % NT == 0, "tile / thread mismatch");
   static_assert(!(KF == FMT_E4M3 && QF == FMT_INT8), "unsupported");
   static_assert(QF == KF || (QF == FMT_BF16 && KF == FMT_E4M3), "unsupported");
 };
@@ -83,33 +87,54 @@ template <> struct QRegs<FMT_BF16> { v8bf r[8]; };  // d = 64g + 8t .. +8, t = 0
 template <> struct QRegs<FMT_E4M3> { v8i r[2]; };   // bytes 64t + 32g .. +32
 template <> struct QRegs<FMT_INT8> { v4i r[4]; };   // bytes 32t + 16g .. +16
 
+template <int MT> struct SAcc { v16f r[2]; };
+template <> struct SAcc<FMT_INT8> { v16i r[2]; };
+
+// Workgroup id -> logical tile.  The dispatcher places workgroup i on XCD
+// i % 8; each XCD receives a contiguous range of logical tiles, so the
+// workgroups resident on one XCD work on the same head at the same time and
+// share its K/V stream in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int i, int total) {
+  const int r = total % 8, per = total / 8;
+  const int x = i % 8, j = i / 8;
+  return x * per + min(x, r) + j;
+}
+
 template <class C>
-__global__ __launch_bounds__(C::NT) void fwd_kernel(FwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int m32 = lane & 31;
 
-  const int b = blockIdx.z;
-  const int hq = blockIdx.y;
+  // ---- which (batch, head, query tile) this workgroup owns
+  const int qtile = 32 * C::NW;
+  const int nqt = (a.Sq + qtile - 1) / qtile;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = lin % nqt;
+  if (a.causal) qt = nqt - 1 - qt;  // longest causal rows first
+  const int bh = lin / nqt;
+  const int hq = bh % a.Hq;
+  const int b = bh / a.Hq;
   const int hk = hq / a.group;
-  const int q0 = blockIdx.x * (32 * C::NW);
+  const int q0 = qt * qtile;
   const int q0w = q0 + 32 * wave;
   const int qi = q0w + m32;                // this lane's query row
   const int causal_off = a.Skv - a.Sq;     // key j visible iff j <= i + causal_off
 
-  // ---- key range of the workgroup and of this wave
+  // ---- key range of the workgroup; sub-tiles needing per-pair masks
   int kv_end = a.Skv;
   if (a.causal) {
-    const int qlast = min(q0 + 32 * C::NW, a.Sq) - 1;
+    const int qlast = min(q0 + qtile, a.Sq) - 1;
     kv_end = min(kv_end, max(qlast + causal_off + 1, 0));
   }
   const int n_sub = (kv_end + kSub - 1) / kSub;
-  int kv_end_w = a.Skv;
-  if (a.causal) kv_end_w = min(kv_end_w, max(min(q0w + 31, a.Sq - 1) + causal_off + 1, 0));
-  const bool wave_live = q0w < a.Sq;
+  // sub-tiles [0, full_end) are valid for every (query, key) pair of the workgroup
+  int full_keys = a.Skv;
+  if (a.causal) full_keys = min(full_keys, max(q0 + causal_off + 1, 0));
+  const int full_end = full_keys / kSub;
 
   const uint8_t* mask_row = nullptr;
   if (C::MASKED) mask_row = a.mask + (int64_t)b * a.m_sb + (int64_t)hq * a.m_sh + (int64_t)(q0 / 64) * a.m_sqb;
@@ -120,7 +145,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdArgs a) {
     return t;
   };
 
-  // ---- global -> register staging of one sub-tile of K and V
+  // ---- HBM -> LDS staging
   const uint8_t* kbase = a.k + (int64_t)hk * a.k_sh;
   const uint8_t* vbase = a.v + (int64_t)hk * a.v_sh;
   const int32_t* pt_row = C::PAGED ? a.page_table + (int64_t)b * a.pt_sb : nullptr;
@@ -129,69 +154,79 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdArgs a) {
     vbase += (int64_t)b * a.v_sb;
   }
   const int page_shift = C::PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
-  auto token_off = [&](int key, const int64_t sb, const int64_t ss, bool& ok) -> int64_t {
-    if (!C::PAGED) {
-      ok = key < a.Skv;
-      return (int64_t)key * ss;
-    }
-    ok = false;
-    if (key >= a.Skv) return 0;
-    const int page = pt_row[key >> page_shift];
-    ok = (unsigned)page < (unsigned)a.num_pages;
-    return ok ? (int64_t)page * sb + (int64_t)(key & (a.page_size - 1)) * ss : 0;
+  // Byte offset of token `key`, clamped into the sequence (rows past the end
+  // load the last token, whose pairs are masked); a page-table entry outside
+  // the pool reads page 0.
+  auto token_off = [&](int key, const int64_t sb, const int64_t ss) -> int64_t {
+    key = min(key, a.Skv - 1);
+    if (!C::PAGED) return (int64_t)key * ss;
+    int page = pt_row[key >> page_shift];
+    page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
+    return (int64_t)page * sb + (int64_t)(key & (a.page_size - 1)) * ss;
   };
-
-  uint4 kreg[C::K_LOADS];
-  uint4 vreg[C::V_LOADS];
-  auto load_tile = [&](int t) {
-    const int kv0 = t * kSub;
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const vbuf0 = smem + 2 * C::K_BUF;
+  // K rows are stored in MFMA row order: LDS row 32T + m holds key 32T + sigma(m).
+  auto dma_k = [&](int t, int buf) {
+    if constexpr (C::K_DMA) {
+      const int kv0 = t * kSub;
+      uint8_t* dst = kbuf0 + buf * C::K_BUF;
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::K_CPR, cc = id % C::K_CPR;
-      bool ok;
-      const int64_t off = token_off(kv0 + row, a.k_sb, a.k_ss, ok);
-      kreg[i] = ok ? *(const uint4*)(kbase + off + cc * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::V_CPR, cc = id % C::V_CPR;
-      bool ok;
-      const int64_t off = token_off(kv0 + row, a.v_sb, a.v_ss, ok);
-      vreg[i] = ok ? *(const uint4*)(vbase + off + cc * 16) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint8_t* ks = smem + stage * C::STAGE;
-    uint8_t* vs = ks + C::K_TILE;
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::K_CPR, cc = id % C::K_CPR;
-      if (C::KF == C::MT) {
-        *(uint4*)(ks + lds_off<C::KROW>(row, cc)) = kreg[i];
-      } else {
-        // E4M3 codes widened to bf16 (exact: 4 significant bits) for the
-        // bf16 x bf16 product with a bf16 Q.
-        uint32_t w[4] = {kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v2f lo = unpack_e4m3<false>((int)w[j]);
-          v2f hi = unpack_e4m3<true>((int)w[j]);
-          o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-          o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-        }
-        *(uint4*)(ks + lds_off<C::KROW>(row, 2 * cc)) = make_uint4(o[0], o[1], o[2], o[3]);
-        *(uint4*)(ks + lds_off<C::KROW>(row, 2 * cc + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+      for (int j = wave; j < C::K_DMA_OPS; j += C::NW) {
+        const int cid = j * 64 + lane;
+        const int row = cid / C::KP_CPR;
+        int ch = cid % C::KP_CPR;
+        ch = ch < C::K_CPR ? ch : 0;  // the pad chunk: any valid bytes
+        const int key = kv0 + 32 * (row >> 5) + sigma(row & 31);
+        const uint8_t* src = kbase + token_off(key, a.k_sb, a.k_ss) + ch * 16;
+        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }
+  };
+  auto dma_v = [&](int t, int buf) {
+    const int kv0 = t * kSub;
+    uint8_t* dst = vbuf0 + buf * C::V_BUF;
 #pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
+    for (int j = wave; j < C::V_DMA_OPS; j += C::NW) {
+      const int cid = j * 64 + lane;
+      const int row = cid / C::VP_CPR;
+      int ch = cid % C::VP_CPR;
+      ch = ch < C::V_CPR ? ch : 0;
+      const uint8_t* src = vbase + token_off(kv0 + row, a.v_sb, a.v_ss) + ch * 16;
+      __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+    }
+  };
+  // Register path for K when its LDS format differs (E4M3 widened to bf16).
+  uint4 kreg[C::K_REG_LOADS > 0 ? C::K_REG_LOADS : 1];
+  auto load_k_regs = [&](int t) {
+    const int kv0 = t * kSub;
+#pragma unroll
+    for (int i = 0; i < C::K_REG_LOADS; ++i) {
       const int id = tid + i * C::NT;
-      const int row = id / C::V_CPR, cc = id % C::V_CPR;
-      *(uint4*)(vs + lds_off<C::VROW>(row, cc)) = vreg[i];
+      const int row = id / C::KG_CPR, cc = id % C::KG_CPR;
+      const int key = kv0 + 32 * (row >> 5) + sigma(row & 31);
+      kreg[i] = *(const uint4*)(kbase + token_off(key, a.k_sb, a.k_ss) + cc * 16);
+    }
+  };
+  auto store_k_regs = [&](int buf) {
+    uint8_t* dst = kbuf0 + buf * C::K_BUF;
+#pragma unroll
+    for (int i = 0; i < C::K_REG_LOADS; ++i) {
+      const int id = tid + i * C::NT;
+      const int row = id / C::KG_CPR, cc = id % C::KG_CPR;
+      // E4M3 codes widened to bf16 (exact: 4 significant bits).
+      uint32_t w[4] = {kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v2f lo = unpack_e4m3<false>((int)w[j]);
+        v2f hi = unpack_e4m3<true>((int)w[j]);
+        o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+        o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+      }
+      uint8_t* rp = dst + row * C::KP + 32 * cc;
+      *(uint4*)(rp) = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)(rp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
     }
   };
 
@@ -226,194 +261,253 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdArgs a) {
   const float log2sp = a.sfs_p ? __log2f(a.sfs_p[hq]) : 0.0f;
   const float* sk_row = C::KS ? a.sfs_k + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
   const float* sv_row = C::VS ? a.sfs_v + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
+  const float c_q = a.scale_log2 * sq;
 
-  // ---- per-lane state: O^T (4 tiles of 32 d x 32 queries), row max, denominator
+  // ---- per-lane LDS read bases (stage-relative; every operand read is a
+  //      fixed immediate offset from these)
+  int kb_lane;
+  if constexpr (C::MT == FMT_BF16) kb_lane = m32 * C::KP + 128 * g;
+  else if constexpr (C::MT == FMT_E4M3) kb_lane = m32 * C::KP + 32 * g;
+  else kb_lane = m32 * C::KP + 16 * g;
+  const int tr_G = lane >> 4;
+  int vb_lane;
+  if constexpr (C::VF == FMT_E4M3)  // source row 16g + r, column 16(G%2) + 8h
+    vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 1)) * C::VP + 16 * (tr_G & 1) + 8 * (lane & 1);
+  else  // bf16 V: source row 16g + r, byte column 32(G%2) + 8h'
+    vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 2)) * C::VP + 32 * (tr_G & 1) + 8 * (lane & 3);
+
+  // S^T for one sub-tile from the K buffer `kb`
+  auto qk = [&](const uint8_t* kb) {
+    SAcc<C::MT> acc;
+    const uint8_t* kp = kb + kb_lane;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const uint8_t* kt = kp + 32 * T * C::KP;
+      if constexpr (C::MT == FMT_BF16) {
+        acc.r[T] = v16f{};
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const uint4 u = *(const uint4*)(kt + 16 * tt);
+          acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, u), q.r[tt], acc.r[T]);
+        }
+      } else if constexpr (C::MT == FMT_E4M3) {
+        acc.r[T] = v16f{};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const uint4 u0 = *(const uint4*)(kt + 64 * tt);
+          const uint4 u1 = *(const uint4*)(kt + 64 * tt + 16);
+          const v8i av = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+          acc.r[T] = mfma_f8(av, q.r[tt], acc.r[T]);
+        }
+      } else {
+        acc.r[T] = v16i{};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const uint4 u = *(const uint4*)(kt + 32 * tt);
+          acc.r[T] = mfma_i8(v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}, q.r[tt], acc.r[T]);
+        }
+      }
+    }
+    return acc;
+  };
+
+  // ---- per-lane state.  O^T (4 tiles of 32 d x 32 queries) is kept in units
+  // of the reference V scale `sv_ref`: before a sub-tile's PV product is
+  // accumulated, O is multiplied by alpha_row * sv_ref / sv_tile (one multiply
+  // folds the lazy rescale and the change of V block scale), then the MFMA
+  // accumulates codes x codes directly.
   v16f o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = v16f{};
   float m_run = -kInf;
   float den = 0.0f;
+  float sv_ref = 1.0f, sv_max = 0.0f;
 
-  // Per-lane LDS offsets of the MFMA operands (stage-relative).
-  const int krow0 = sigma(m32);  // K row of this lane in tile T = 0 (T = 1 adds 32 rows)
-  // V^T transposing reads: source lane supplies row key(c, r) and column block.
-  const int tr_G = lane >> 4;
-  const int tr_g = tr_G >> 1;
-
-  // ---- main loop over 64-key sub-tiles
-  int t = next_sub(0);
-  if (t < n_sub) {
-    load_tile(t);
-    store_tile(0);
-  }
-  __syncthreads();
-  int stage = 0;
-  while (t < n_sub) {
-    const int tn = next_sub(t + 1);
-    if (tn < n_sub) load_tile(tn);
+  // softmax + P requantisation + PV for sub-tile t from S^T `acc` and V buffer `vb`
+  auto softmax_pv = [&](const SAcc<C::MT>& acc, int t, const uint8_t* vb, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int kv0 = t * kSub;
-    if (wave_live && kv0 < kv_end_w) {
-      const uint8_t* ks = smem + stage * C::STAGE;
-      const uint8_t* vs = ks + C::K_TILE;
-      // -- S^T = K Q^T for the two 32-key tiles
-      float s[32];
-      if constexpr (C::MT == FMT_INT8) {
-        v16i acc[2] = {v16i{}, v16i{}};
+    float s[32];
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          const int row = 32 * T + krow0;
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            uint4 u = *(const uint4*)(ks + lds_off<C::KROW>(row, 2 * tt + g));
-            acc[T] = mfma_i8(v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}, q.r[tt], acc[T]);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 32; ++e) s[e] = (float)acc[e >> 4][e & 15];
-      } else {
-        v16f acc[2] = {v16f{}, v16f{}};
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          const int row = 32 * T + krow0;
-          if constexpr (C::MT == FMT_BF16) {
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-              uint4 u = *(const uint4*)(ks + lds_off<C::KROW>(row, 8 * g + tt));
-              acc[T] = mfma_bf16(__builtin_bit_cast(v8bf, u), q.r[tt], acc[T]);
-            }
-          } else {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              uint4 u0 = *(const uint4*)(ks + lds_off<C::KROW>(row, 4 * tt + 2 * g));
-              uint4 u1 = *(const uint4*)(ks + lds_off<C::KROW>(row, 4 * tt + 2 * g + 1));
-              v8i av = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-              acc[T] = mfma_f8(av, q.r[tt], acc[T]);
-            }
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 32; ++e) s[e] = acc[e >> 4][e & 15];
-      }
-      // -- validity of (query, key) pairs on edge sub-tiles: s[e] is key
-      //    kv0 + 32*(e/16) + 16*g + e%16
-      const bool edge = (kv0 + kSub > a.Skv) || (a.causal && kv0 + kSub - 1 > q0w + causal_off);
-      if (edge) {
-        const int lim = a.causal ? min(a.Skv, qi + causal_off + 1) : a.Skv;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const int key = kv0 + 32 * (e >> 4) + 16 * g + (e & 15);
-          if (key >= lim) s[e] = -kInf;
-        }
-      }
-      // -- row maximum (raw units), lazy decision (log2 units)
-      float mx = s[0];
-#pragma unroll
-      for (int e = 1; e < 32; ++e) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float c = a.scale_log2 * sq;
-      if (C::KS) c *= sk_row[t];
-      const float tmax = mx * c;  // c > 0, so the maximum commutes with the scale
-      const bool trig = (tmax != -kInf) && (m_run == -kInf || tmax - m_run > a.tau);
-      if (__ballot(trig) != 0) {
-        const float alpha = trig ? (m_run == -kInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax)) : 1.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-        den *= alpha;
-        if (trig) m_run = tmax;
-      }
-      const float negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
-      float p[32];
+    for (int e = 0; e < 32; ++e) s[e] = (float)acc.r[e >> 4][e & 15];
+    if constexpr (EDGE) {
+      // s[e] is key kv0 + 32(e/16) + 16g + e%16
+      const int lim = a.causal ? min(a.Skv, qi + causal_off + 1) : a.Skv;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm));
-        if (C::VF == FMT_E4M3 && a.clamp_p) p[e] = fminf(p[e], 448.0f);
+        const int key = kv0 + 32 * (e >> 4) + 16 * g + (e & 15);
+        s[e] = key < lim ? s[e] : -kInf;
       }
-      // -- P to the PV operand format, denominator from the quantised values,
-      //    then O^T += V^T P^T
-      if constexpr (C::VF == FMT_E4M3) {
-        v8i pb;
-        float dsum = 0.0f;
+    }
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          int pk = pack_e4m3<false>(p[4 * w], p[4 * w + 1], 0);
-          pk = pack_e4m3<true>(p[4 * w + 2], p[4 * w + 3], pk);
-          pb[w] = pk;
-          const v2f lo = unpack_e4m3<false>(pk);
-          const v2f hi = unpack_e4m3<true>(pk);
-          dsum += (lo.x + lo.y) + (hi.x + hi.y);
+    for (int e = 2; e < 32; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float c = C::KS ? c_q * sk_row[t] : c_q;
+    const float tmax = mx * c;  // c > 0, so the maximum commutes with the scale
+    const bool trig = (tmax != -kInf) && (m_run == -kInf || tmax - m_run > a.tau);
+    const float alpha = trig ? (m_run == -kInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax)) : 1.0f;
+    m_run = trig ? tmax : m_run;
+    den *= alpha;
+    const float negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
+    // V-scale bookkeeping (wave-uniform)
+    float fo = alpha;  // factor applied to O before the MFMA accumulates
+    bool direct = true;
+    float sv_t = 1.0f;
+    if constexpr (C::VS) {
+      sv_t = sv_row[t];
+      sv_max = fmaxf(sv_max, sv_t);
+      // keep |O| bounded: move the reference only while the largest scale
+      // seen stays within 2^48 of it
+      direct = sv_max <= sv_t * 0x1p48f;
+      if (direct) {
+        fo = alpha * (sv_ref / sv_t);
+        sv_ref = sv_t;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= fo;
+    // P = 2^(s2 - m) / sp
+    bool clamp = false;
+    if (C::VF == FMT_E4M3 && a.clamp_p) clamp = __ballot(tmax - m_run - log2sp > 8.5f) != 0;
+    if (clamp) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) s[e] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm)), 448.0f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm));
+    }
+    if constexpr (C::VF == FMT_E4M3) {
+      v8i pb;
+      float dsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        int pk = pack_e4m3<false>(s[4 * w], s[4 * w + 1], 0);
+        pk = pack_e4m3<true>(s[4 * w + 2], s[4 * w + 3], pk);
+        pb[w] = pk;
+        const v2f lo = unpack_e4m3<false>(pk);
+        const v2f hi = unpack_e4m3<true>(pk);
+        dsum += (lo.x + lo.y) + (hi.x + hi.y);
+      }
+      den += dsum;
+      const uint8_t* vp = vb + vb_lane;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v8i av;
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+          // rows 32(cq/2) + 8(cq%2) further down, columns 32d further right
+          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
+          av[2 * cq] = r[0];
+          av[2 * cq + 1] = r[1];
         }
-        den += dsum;
-        const float svv = C::VS ? sv_row[t] : 1.0f;
+        if (direct) {
+          o[d] = mfma_f8(av, pb, o[d]);
+        } else {
+          const v16f part = mfma_f8(av, pb, v16f{});
+          const float f = sv_t / sv_ref;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          v8i av;
-#pragma unroll
-          for (int cq = 0; cq < 4; ++cq) {
-            // source row: key 32(cq/2) + 16 g + 8(cq%2) + r, column 32d + 16(G%2) + 8h
-            const int row = 32 * (cq >> 1) + 16 * tr_g + 8 * (cq & 1) + ((lane & 15) >> 1);
-            const int off = lds_off<128>(row, 2 * d + (tr_G & 1)) + 8 * (lane & 1);
-            const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(FMHA_LDS(v2i, vs + off));
-            av[2 * cq] = r[0];
-            av[2 * cq + 1] = r[1];
-          }
-          if (C::VS) {
-            const v16f part = mfma_f8(av, pb, v16f{});
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], svv, o[d][r]);
-          } else {
-            o[d] = mfma_f8(av, pb, o[d]);
-          }
+          for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], f, o[d][r]);
         }
-      } else {
-        // bf16 P and V (V unscaled).
-        v8bf pbf[4];
-        float dsum = 0.0f;
+      }
+    } else {
+      // bf16 P and V (V unscaled).
+      v8bf pbf[4];
+      float dsum = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = f32_to_bf16_bits(s[8 * kk + 2 * j]);
+          const uint32_t hi = f32_to_bf16_bits(s[8 * kk + 2 * j + 1]);
+          w[j] = lo | (hi << 16);
+          dsum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+        }
+        pbf[kk] = __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      den += dsum;
+      const uint8_t* vp = vb + vb_lane;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           uint32_t w[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = f32_to_bf16_bits(p[8 * kk + 2 * j]);
-            const uint32_t hi = f32_to_bf16_bits(p[8 * kk + 2 * j + 1]);
-            w[j] = lo | (hi << 16);
-            dsum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+          for (int cq = 0; cq < 2; ++cq) {
+            // rows 32(kk/2) + 8(kk%2) + 4cq further down, columns 64d bytes right
+            const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                FMHA_LDS(v4s, vp + (32 * (kk >> 1) + 8 * (kk & 1) + 4 * cq) * C::VP + 64 * d));
+            w[2 * cq] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+            w[2 * cq + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
           }
-          pbf[kk] = __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
-        }
-        den += dsum;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            uint32_t w[4];
-#pragma unroll
-            for (int cq = 0; cq < 2; ++cq) {
-              // source row: key 32(kk/2) + 16 g + 8(kk%2) + 4 cq + r, halfword
-              // column 32d + 16(G%2) + 4h'
-              const int row = 32 * (kk >> 1) + 16 * tr_g + 8 * (kk & 1) + 4 * cq + ((lane & 15) >> 2);
-              const int hp = lane & 3;
-              const int off = lds_off<256>(row, 4 * d + 2 * (tr_G & 1) + (hp >> 1)) + 8 * (hp & 1);
-              const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FMHA_LDS(v4s, vs + off));
-              w[2 * cq] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
-              w[2 * cq + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
-            }
-            o[d] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), pbf[kk], o[d]);
-          }
+          o[d] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), pbf[kk], o[d]);
         }
       }
     }
-    if (tn < n_sub) store_tile(stage ^ 1);
-    __syncthreads();
-    stage ^= 1;
-    t = tn;
+  };
+
+  // ---- main loop.  K runs one sub-tile ahead of V: iteration i computes
+  // S^T of the next sub-tile (MFMA) while the softmax of the current one runs
+  // (VALU), then the current PV product.  Buffers: K(next) and V(cur) are
+  // read while K(after next) and V(next) land.
+  int tc = next_sub(0);
+  int tn = tc < n_sub ? next_sub(tc + 1) : n_sub;
+  if (tc < n_sub) {
+    dma_k(tc, 0);
+    dma_v(tc, 0);
+    if constexpr (!C::K_DMA) {
+      load_k_regs(tc);
+      store_k_regs(0);
+    }
+    if (tn < n_sub) {
+      dma_k(tn, 1);
+      if constexpr (!C::K_DMA) {
+        load_k_regs(tn);
+        store_k_regs(1);
+      }
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  __syncthreads();
+  SAcc<C::MT> s_cur{};
+  if (tc < n_sub) s_cur = qk(kbuf0);
+  __syncthreads();  // K buffer 0 is rewritten below
+  int kcur = 0;     // K buffer of tc (now free); tn sits in kcur ^ 1
+  int vcur = 0;     // V buffer of tc
+  auto step = [&](auto edge_tag) {
+    const int tnn = tn < n_sub ? next_sub(tn + 1) : n_sub;
+    if (tnn < n_sub) {
+      dma_k(tnn, kcur);
+      if constexpr (!C::K_DMA) load_k_regs(tnn);
+    }
+    if (tn < n_sub) dma_v(tn, vcur ^ 1);
+    SAcc<C::MT> s_next{};
+    if (tn < n_sub) s_next = qk(kbuf0 + (kcur ^ 1) * C::K_BUF);
+    softmax_pv(s_cur, tc, vbuf0 + vcur * C::V_BUF, edge_tag);
+    if constexpr (!C::K_DMA) {
+      if (tnn < n_sub) store_k_regs(kcur);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+    s_cur = s_next;
+    kcur ^= 1;
+    vcur ^= 1;
+    tc = tn;
+    tn = tnn;
+  };
+  // sub-tiles valid for every pair of the workgroup first, then the edge ones
+  if constexpr (!C::MASKED) {
+    while (tc < n_sub && tc < full_end) step(std::false_type{});
+  }
+  while (tc < n_sub) step(std::true_type{});
 
   // ---- epilogue: O = num / den in bf16; rows without a valid key give 0
-  if (!wave_live) return;
   const float dt = den + __shfl_xor(den, 32, 64);
-  const float inv = dt > 0.0f ? 1.0f / dt : 0.0f;
+  const float inv = dt > 0.0f ? sv_ref / dt : 0.0f;
   if (qi >= a.Sq) return;
   uint8_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)qi * a.o_ss;
 #pragma unroll
@@ -433,8 +527,10 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdArgs a) {
 template <class C>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int qtile = 32 * C::NW;
-  dim3 grid((unsigned)((a.Sq + qtile - 1) / qtile), (unsigned)a.Hq, (unsigned)a.B);
-  const size_t lds = 2 * (size_t)C::STAGE;
+  const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles);
+  const size_t lds = (size_t)C::LDS_BYTES;
   static bool configured = false;  // benign race: the attribute is idempotent
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -463,8 +559,8 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
     if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, true, true, 2>>(a, s);
     return launch<Cfg<QF, KF, VF, QS, KS, VS, true, false, 2>>(a, s);
   }
-  if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, 4>>(a, s);
-  return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, 4>>(a, s);
+  if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves>>(a, s);
+  return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves>>(a, s);
 }
 
 hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
