@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kSub = 64;  // keys per sub-tile: lazy-decision and V-scale unit
 #ifndef FMHA_DENSE_WAVES
-#define FMHA_DENSE_WAVES 8
+#define FMHA_DENSE_WAVES 4
 #endif
 constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per dense workgroup
 constexpr float kInf = __builtin_huge_valf();
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;
   const int m32 = lane & 31;
 
@@ -321,11 +321,33 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   for (int d = 0; d < 4; ++d) o[d] = v16f{};
   float m_run = -kInf;
   float den = 0.0f;
-  float sv_ref = 1.0f, sv_max = 0.0f;
+  float sv_ref = 1.0f;
+
+  // V-scale reference (wave-uniform).  The fast path moves the reference to
+  // every sub-tile's own scale, so the MFMA accumulates codes x codes straight
+  // into O; it is taken when all V block scales of this (batch, KV head) lie
+  // within 2^64 of each other, which bounds |O| far below the fp32 range.
+  // Otherwise each sub-tile's product goes through a zeroed accumulator and is
+  // added with its scale relative to the reference.
+  bool v_direct = true;
+  if constexpr (C::VS) {
+    float lo = kInf, hi = 0.0f;
+    for (int i = lane; i < a.nblk_kv; i += 64) {
+      const float v = sv_row[i];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    lo = -wave_max(-lo);
+    hi = wave_max(hi);
+    v_direct = hi <= lo * 0x1p64f;
+  }
 
   // softmax + P requantisation + PV for sub-tile t from S^T `acc` and V buffer `vb`
-  auto softmax_pv = [&](const SAcc<C::MT>& acc, int t, const uint8_t* vb, auto edge_tag) {
+  auto softmax_pv = [&](const SAcc<C::MT>& acc, int t, const uint8_t* vb, auto edge_tag, auto clamp_tag,
+                        auto direct_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr bool CLAMP = decltype(clamp_tag)::value;
+    constexpr bool DIRECT = decltype(direct_tag)::value;
     const int kv0 = t * kSub;
     float s[32];
 #pragma unroll
@@ -350,34 +372,29 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     m_run = trig ? tmax : m_run;
     den *= alpha;
     const float negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
-    // V-scale bookkeeping (wave-uniform)
-    float fo = alpha;  // factor applied to O before the MFMA accumulates
-    bool direct = true;
-    float sv_t = 1.0f;
-    if constexpr (C::VS) {
-      sv_t = sv_row[t];
-      sv_max = fmaxf(sv_max, sv_t);
-      // keep |O| bounded: move the reference only while the largest scale
-      // seen stays within 2^48 of it
-      direct = sv_max <= sv_t * 0x1p48f;
-      if (direct) {
-        fo = alpha * (sv_ref / sv_t);
-        sv_ref = sv_t;
+    // Rescale O: lazy factor and (fast path) change of V reference scale.
+    const float sv_t = C::VS ? sv_row[t] : 1.0f;
+    if constexpr (C::VS && DIRECT) {
+      const float fo = alpha * (sv_ref / sv_t);
+      sv_ref = sv_t;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= fo;
+    } else {
+      if (__ballot(trig) != 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
     }
+    // P = 2^(s2 - m) / sp, clamped to the E4M3 range only where P / sp can
+    // reach it (sfs_p given or tau above log2(448))
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= fo;
-    // P = 2^(s2 - m) / sp
-    bool clamp = false;
-    if (C::VF == FMT_E4M3 && a.clamp_p) clamp = __ballot(tmax - m_run - log2sp > 8.5f) != 0;
-    if (clamp) {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) s[e] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm)), 448.0f);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm));
+    for (int e = 0; e < 32; ++e) {
+      s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm));
+      if constexpr (CLAMP) s[e] = fminf(s[e], 448.0f);
     }
     if constexpr (C::VF == FMT_E4M3) {
       v8i pb;
@@ -393,22 +410,27 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       den += dsum;
       const uint8_t* vp = vb + vb_lane;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      // V^T operand of d-tile `d`: rows 32(cq/2) + 8(cq%2) further down,
+      // columns 32d further right of the lane's base
+      auto v_operand = [&](int d) {
         v8i av;
 #pragma unroll
         for (int cq = 0; cq < 4; ++cq) {
-          // rows 32(cq/2) + 8(cq%2) further down, columns 32d further right
           const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
           av[2 * cq] = r[0];
           av[2 * cq + 1] = r[1];
         }
-        if (direct) {
-          o[d] = mfma_f8(av, pb, o[d]);
-        } else {
-          const v16f part = mfma_f8(av, pb, v16f{});
-          const float f = sv_t / sv_ref;
+        return av;
+      };
+      if constexpr (!C::VS || DIRECT) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = mfma_f8(v_operand(d), pb, o[d]);
+      } else {
+        const float f = sv_t / sv_ref;  // reference stays at 1
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const v16f part = mfma_f8(v_operand(d), pb, v16f{});
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], f, o[d][r]);
         }
@@ -450,12 +472,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     }
   };
 
-  // ---- main loop.  K runs one sub-tile ahead of V: iteration i computes
-  // S^T of the next sub-tile (MFMA) while the softmax of the current one runs
-  // (VALU), then the current PV product.  Buffers: K(next) and V(cur) are
-  // read while K(after next) and V(next) land.
+  // ---- main loop over 64-key sub-tiles, K/V double-buffered in LDS.  Per
+  // sub-tile a wave runs S^T = K Q^T (MFMA), the softmax (VALU), then
+  // O^T += V^T P^T (MFMA); an MFMA holds its wave's issue for its whole
+  // duration on this hardware, so MFMA/VALU overlap comes from the second
+  // wave on the SIMD (another workgroup) being in the opposite phase.
   int tc = next_sub(0);
-  int tn = tc < n_sub ? next_sub(tc + 1) : n_sub;
   if (tc < n_sub) {
     dma_k(tc, 0);
     dma_v(tc, 0);
@@ -463,47 +485,47 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       load_k_regs(tc);
       store_k_regs(0);
     }
-    if (tn < n_sub) {
-      dma_k(tn, 1);
-      if constexpr (!C::K_DMA) {
-        load_k_regs(tn);
-        store_k_regs(1);
-      }
-    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
-  SAcc<C::MT> s_cur{};
-  if (tc < n_sub) s_cur = qk(kbuf0);
-  __syncthreads();  // K buffer 0 is rewritten below
-  int kcur = 0;     // K buffer of tc (now free); tn sits in kcur ^ 1
-  int vcur = 0;     // V buffer of tc
-  auto step = [&](auto edge_tag) {
-    const int tnn = tn < n_sub ? next_sub(tn + 1) : n_sub;
-    if (tnn < n_sub) {
-      dma_k(tnn, kcur);
-      if constexpr (!C::K_DMA) load_k_regs(tnn);
+  int buf = 0;
+  auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
+    const int tn = next_sub(tc + 1);
+    if (tn < n_sub) {
+      dma_k(tn, buf ^ 1);
+      dma_v(tn, buf ^ 1);
+      if constexpr (!C::K_DMA) load_k_regs(tn);
     }
-    if (tn < n_sub) dma_v(tn, vcur ^ 1);
-    SAcc<C::MT> s_next{};
-    if (tn < n_sub) s_next = qk(kbuf0 + (kcur ^ 1) * C::K_BUF);
-    softmax_pv(s_cur, tc, vbuf0 + vcur * C::V_BUF, edge_tag);
+    const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF);
+    softmax_pv(acc, tc, vbuf0 + buf * C::V_BUF, edge_tag, clamp_tag, direct_tag);
     if constexpr (!C::K_DMA) {
-      if (tnn < n_sub) store_k_regs(kcur);
+      if (tn < n_sub) store_k_regs(buf ^ 1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
     __syncthreads();
-    s_cur = s_next;
-    kcur ^= 1;
-    vcur ^= 1;
+    buf ^= 1;
     tc = tn;
-    tn = tnn;
   };
-  // sub-tiles valid for every pair of the workgroup first, then the edge ones
-  if constexpr (!C::MASKED) {
-    while (tc < n_sub && tc < full_end) step(std::false_type{});
+  auto run = [&](auto clamp_tag, auto direct_tag) {
+    // sub-tiles valid for every pair of the workgroup first, then the edge ones
+    if constexpr (!C::MASKED) {
+      while (tc < n_sub && tc < full_end) step(std::false_type{}, clamp_tag, direct_tag);
+    }
+    while (tc < n_sub) step(std::true_type{}, clamp_tag, direct_tag);
+  };
+  const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;
+  if constexpr (C::VS) {
+    if (clamp) {
+      if (v_direct) run(std::true_type{}, std::true_type{});
+      else run(std::true_type{}, std::false_type{});
+    } else {
+      if (v_direct) run(std::false_type{}, std::true_type{});
+      else run(std::false_type{}, std::false_type{});
+    }
+  } else {
+    if (clamp) run(std::true_type{}, std::true_type{});
+    else run(std::false_type{}, std::true_type{});
   }
-  while (tc < n_sub) step(std::true_type{});
 
   // ---- epilogue: O = num / den in bf16; rows without a valid key give 0
   const float dt = den + __shfl_xor(den, 32, 64);
