@@ -12,7 +12,8 @@ import ctypes
 import math
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfmha.so")
+# FMHA_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("FMHA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfmha.so")
 
 FMHA_DT_BF16, FMHA_DT_E4M3, FMHA_DT_INT8 = 1, 2, 3
 FMHA_OK, FMHA_ERR_INVALID, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP = 0, -1, -2, -3

@@ -152,6 +152,10 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
     if (p->page_table_stride_b < 0) return fail(FMHA_ERR_INVALID, "fwd: negative page_table_stride_b");
   }
   if (p->sfs_p && reinterpret_cast<uintptr_t>(p->sfs_p) % 4) return fail(FMHA_ERR_INVALID, "fwd: sfs_p misaligned");
+  // one 64-token tile of K or V must span less than 2 GiB (32-bit in-tile offsets)
+  if (p->k.stride_s * elem_size(p->k.dtype) >= (int64_t(1) << 25) ||
+      p->v.stride_s * elem_size(p->v.dtype) >= (int64_t(1) << 25))
+    return fail(FMHA_ERR_UNSUPPORTED, "fwd: K/V token stride of 32 MiB or more");
 
   fmha::FwdKey key{};
   key.qf = to_fmt(p->q.dtype);

@@ -44,6 +44,9 @@ constexpr int kSub = 64;  // keys per sub-tile: lazy-decision and V-scale unit
 #define FMHA_DENSE_WAVES 4
 #endif
 constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per dense workgroup
+#ifndef FMHA_WAVES_PER_EU
+#define FMHA_WAVES_PER_EU 2  // register budget: 512 / 2 VGPRs per lane
+#endif
 constexpr float kInf = __builtin_huge_valf();
 
 // Key held by row m of a 32-key MFMA tile: lane group g of the S^T result
@@ -101,7 +104,8 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVES_PER_EU))) void fwd_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,34 +170,82 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   };
   uint8_t* const kbuf0 = smem;
   uint8_t* const vbuf0 = smem + 2 * C::K_BUF;
-  // K rows are stored in MFMA row order: LDS row 32T + m holds key 32T + sigma(m).
+  // Every wave issues the same number of wave-wide DMA operations per
+  // sub-tile (slots past the tile repeat its last operation: identical bytes
+  // to the same place), so the loop body has no per-wave branches.  Per-lane
+  // source offsets within a tile are fixed; contiguous K/V go through a
+  // buffer resource whose range ends at the last token, so rows past the end
+  // of the sequence read as zeros.  K rows are stored in MFMA row order: LDS
+  // row 32T + m holds key 32T + sigma(m).
+  constexpr int KSL = C::K_DMA ? (C::K_DMA_OPS + C::NW - 1) / C::NW : 0;
+  constexpr int VSL = (C::V_DMA_OPS + C::NW - 1) / C::NW;
+  uint32_t k_src[KSL > 0 ? KSL : 1], v_src[VSL];
+  int k_row[KSL > 0 ? KSL : 1], v_row[VSL];  // key within the tile (paged path)
+#pragma unroll
+  for (int sl = 0; sl < KSL; ++sl) {
+    const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+    const int cid = j * 64 + lane;
+    const int row = cid / C::KP_CPR;
+    int ch = cid % C::KP_CPR;
+    ch = ch < C::K_CPR ? ch : 0;  // the pad chunk: any valid bytes
+    k_row[sl] = 32 * (row >> 5) + sigma(row & 31);
+    k_src[sl] = (uint32_t)(k_row[sl] * a.k_ss) + ch * 16;
+    if (C::PAGED) k_src[sl] = ch * 16;
+  }
+#pragma unroll
+  for (int sl = 0; sl < VSL; ++sl) {
+    const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
+    const int cid = j * 64 + lane;
+    const int row = cid / C::VP_CPR;
+    int ch = cid % C::VP_CPR;
+    ch = ch < C::V_CPR ? ch : 0;
+    v_row[sl] = row;
+    v_src[sl] = (uint32_t)(row * a.v_ss) + ch * 16;
+    if (C::PAGED) v_src[sl] = ch * 16;
+  }
+  auto tile_rsrc = [&](const uint8_t* base, int64_t ss, int kv0) {
+    const uint64_t rem = (uint64_t)(a.Skv - kv0) * (uint64_t)ss;
+    const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * ss), 0, nrec, 0x00020000);
+  };
   auto dma_k = [&](int t, int buf) {
     if constexpr (C::K_DMA) {
       const int kv0 = t * kSub;
       uint8_t* dst = kbuf0 + buf * C::K_BUF;
+      if constexpr (!C::PAGED) {
+        const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
 #pragma unroll
-      for (int j = wave; j < C::K_DMA_OPS; j += C::NW) {
-        const int cid = j * 64 + lane;
-        const int row = cid / C::KP_CPR;
-        int ch = cid % C::KP_CPR;
-        ch = ch < C::K_CPR ? ch : 0;  // the pad chunk: any valid bytes
-        const int key = kv0 + 32 * (row >> 5) + sigma(row & 31);
-        const uint8_t* src = kbase + token_off(key, a.k_sb, a.k_ss) + ch * 16;
-        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+        for (int sl = 0; sl < KSL; ++sl) {
+          const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < KSL; ++sl) {
+          const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+          const uint8_t* src = kbase + token_off(kv0 + k_row[sl], a.k_sb, a.k_ss) + k_src[sl];
+          __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+        }
       }
     }
   };
   auto dma_v = [&](int t, int buf) {
     const int kv0 = t * kSub;
     uint8_t* dst = vbuf0 + buf * C::V_BUF;
+    if constexpr (!C::PAGED) {
+      const auto rs = tile_rsrc(vbase, a.v_ss, kv0);
 #pragma unroll
-    for (int j = wave; j < C::V_DMA_OPS; j += C::NW) {
-      const int cid = j * 64 + lane;
-      const int row = cid / C::VP_CPR;
-      int ch = cid % C::VP_CPR;
-      ch = ch < C::V_CPR ? ch : 0;
-      const uint8_t* src = vbase + token_off(kv0 + row, a.v_sb, a.v_ss) + ch * 16;
-      __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+      for (int sl = 0; sl < VSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < VSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
+        const uint8_t* src = vbase + token_off(kv0 + v_row[sl], a.v_sb, a.v_ss) + v_src[sl];
+        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+      }
     }
   };
   // Register path for K when its LDS format differs (E4M3 widened to bf16).
@@ -261,6 +313,23 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const float log2sp = a.sfs_p ? __log2f(a.sfs_p[hq]) : 0.0f;
   const float* sk_row = C::KS ? a.sfs_k + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
   const float* sv_row = C::VS ? a.sfs_v + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
+  // K/V block scales of 64 consecutive sub-tiles live in one VGPR each (lane
+  // i holds sub-tile base + i); a sub-tile's scale is read with readlane.
+  int sc_base = -(1 << 30);
+  float sk_cache = 1.0f, sv_cache = 1.0f;
+  float sk_t = 1.0f, sv_t = 1.0f;  // scales of the current sub-tile (uniform)
+  auto fetch_scales = [&](int t) {
+    if constexpr (C::KS || C::VS) {
+      if (t - sc_base >= 64) {
+        sc_base = t;
+        const int i = min(t + lane, a.nblk_kv - 1);
+        if (C::KS) sk_cache = sk_row[i];
+        if (C::VS) sv_cache = sv_row[i];
+      }
+      if (C::KS) sk_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sk_cache), t - sc_base));
+      if (C::VS) sv_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv_cache), t - sc_base));
+    }
+  };
   const float c_q = a.scale_log2 * sq;
 
   // ---- per-lane LDS read bases (stage-relative; every operand read is a
@@ -365,15 +434,16 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int e = 2; e < 32; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float c = C::KS ? c_q * sk_row[t] : c_q;
+    const float c = C::KS ? c_q * sk_t : c_q;
     const float tmax = mx * c;  // c > 0, so the maximum commutes with the scale
     const bool trig = (tmax != -kInf) && (m_run == -kInf || tmax - m_run > a.tau);
-    const float alpha = trig ? (m_run == -kInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax)) : 1.0f;
+    // 2^(m - t) is 0 for an unset m (m = -inf); rows that do not trigger keep 1
+    const float e_mt = __builtin_amdgcn_exp2f(m_run - tmax);
+    const float alpha = trig ? e_mt : 1.0f;
     m_run = trig ? tmax : m_run;
     den *= alpha;
     const float negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
     // Rescale O: lazy factor and (fast path) change of V reference scale.
-    const float sv_t = C::VS ? sv_row[t] : 1.0f;
     if constexpr (C::VS && DIRECT) {
       const float fo = alpha * (sv_ref / sv_t);
       sv_ref = sv_t;
@@ -490,6 +560,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   __syncthreads();
   int buf = 0;
   auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
+    fetch_scales(tc);
     const int tn = next_sub(tc + 1);
     if (tn < n_sub) {
       dma_k(tn, buf ^ 1);
@@ -544,6 +615,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       *(uint2*)(op + 2 * dd) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
     }
   }
+#endif
 }
 
 template <class C>
