@@ -345,34 +345,67 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   else  // bf16 V: source row 16g + r, byte column 32(G%2) + 8h'
     vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 2)) * C::VP + 32 * (tr_G & 1) + 8 * (lane & 3);
 
-  // S^T for one sub-tile from the K buffer `kb`
+  // S^T for one sub-tile from the K buffer `kb`.  All K operand reads are
+  // issued before the first MFMA, so each MFMA waits only for its own operand
+  // and the LDS latency hides behind the MFMAs ahead of it.
   auto qk = [&](const uint8_t* kb) {
     SAcc<C::MT> acc;
     const uint8_t* kp = kb + kb_lane;
+    if constexpr (C::MT == FMT_BF16 && C::PAGED) {
+      // (register-lean variant for the paged path, whose address state
+      // already takes more registers)
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const uint8_t* kt = kp + 32 * T * C::KP;
-      if constexpr (C::MT == FMT_BF16) {
+      for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
-          const uint4 u = *(const uint4*)(kt + 16 * tt);
+          const uint4 u = *(const uint4*)(kp + 32 * T * C::KP + 16 * tt);
           acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, u), q.r[tt], acc.r[T]);
         }
-      } else if constexpr (C::MT == FMT_E4M3) {
+      }
+    } else if constexpr (C::MT == FMT_BF16) {
+      uint4 kr[2][8];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) kr[T][tt] = *(const uint4*)(kp + 32 * T * C::KP + 16 * tt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        acc.r[T] = v16f{};
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[T][tt]), q.r[tt], acc.r[T]);
+      }
+    } else if constexpr (C::MT == FMT_E4M3) {
+      uint4 kr[2][4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kr[T][i] = *(const uint4*)(kp + 32 * T * C::KP + 64 * (i >> 1) + 16 * (i & 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const uint4 u0 = *(const uint4*)(kt + 64 * tt);
-          const uint4 u1 = *(const uint4*)(kt + 64 * tt + 16);
+          const uint4 u0 = kr[T][2 * tt], u1 = kr[T][2 * tt + 1];
           const v8i av = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           acc.r[T] = mfma_f8(av, q.r[tt], acc.r[T]);
         }
-      } else {
+      }
+    } else {
+      uint4 kr[2][4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) kr[T][tt] = *(const uint4*)(kp + 32 * T * C::KP + 32 * tt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16i{};
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const uint4 u = *(const uint4*)(kt + 32 * tt);
+          const uint4 u = kr[T][tt];
           acc.r[T] = mfma_i8(v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}, q.r[tt], acc.r[T]);
         }
       }
@@ -418,6 +451,25 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     constexpr bool CLAMP = decltype(clamp_tag)::value;
     constexpr bool DIRECT = decltype(direct_tag)::value;
     const int kv0 = t * kSub;
+    // V^T operands of the four d-tiles, read before the softmax so their LDS
+    // latency hides behind it: rows 32(cq/2) + 8(cq%2) further down and
+    // columns 32d further right of the lane's base
+    // (hoisted only where registers allow it: the bf16-QK contiguous path)
+    constexpr bool HOIST_V = C::VF == FMT_E4M3 && C::MT == FMT_BF16 && !C::PAGED;
+    v8i vop[4];
+    auto read_v = [&]() {
+      const uint8_t* vp = vb + vb_lane;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
+          vop[d][2 * cq] = r[0];
+          vop[d][2 * cq + 1] = r[1];
+        }
+    };
+    if constexpr (HOIST_V) read_v();
     float s[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) s[e] = (float)acc.r[e >> 4][e & 15];
@@ -479,28 +531,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
         dsum += (lo.x + lo.y) + (hi.x + hi.y);
       }
       den += dsum;
-      const uint8_t* vp = vb + vb_lane;
-      // V^T operand of d-tile `d`: rows 32(cq/2) + 8(cq%2) further down,
-      // columns 32d further right of the lane's base
-      auto v_operand = [&](int d) {
-        v8i av;
-#pragma unroll
-        for (int cq = 0; cq < 4; ++cq) {
-          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
-          av[2 * cq] = r[0];
-          av[2 * cq + 1] = r[1];
-        }
-        return av;
-      };
+      if constexpr (!HOIST_V) read_v();
       if constexpr (!C::VS || DIRECT) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = mfma_f8(v_operand(d), pb, o[d]);
+        for (int d = 0; d < 4; ++d) o[d] = mfma_f8(vop[d], pb, o[d]);
       } else {
         const float f = sv_t / sv_ref;  // reference stays at 1
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const v16f part = mfma_f8(v_operand(d), pb, v16f{});
+          const v16f part = mfma_f8(vop[d], pb, v16f{});
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], f, o[d][r]);
         }
