@@ -103,6 +103,22 @@ def cpu_baseline(spec, data, budget_s=12.0):
             "seconds": round(t_att, 2)}
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(torch, steps):
+    """A plain copy of COPY_BYTES (read once, written once) for the byte
+    counters: FETCH_SIZE / WRITE_SIZE of this kernel against COPY_BYTES give
+    the scale of the counter readings of the attention kernel."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": max(steps, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the attention of each (batch, head) is independent, so a multi-GPU "
@@ -117,6 +135,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.steps)
+        return
     import fmha_fwd_amd as F
     from fmha_fwd_amd import workloads as W
 

@@ -55,6 +55,15 @@ __device__ __forceinline__ int sigma(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_>
 struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
@@ -63,11 +72,13 @@ struct Cfg {
   static constexpr int KROW = MT == FMT_BF16 ? 256 : 128;        // bytes per K row (LDS format)
   static constexpr int VROW = VF == FMT_BF16 ? 256 : 128;
   static constexpr int KGROW = KF == FMT_BF16 ? 256 : 128;       // bytes per K row in HBM
-  // LDS rows are padded by one 16-byte chunk: consecutive rows start one
-  // chunk apart in the 64 x 4-byte banks, so the 16 rows an MFMA operand read
-  // touches at a time, and the 8 rows of a transposing read, hit distinct banks
-  // while every lane reads at a fixed offset from its own base address.
-  static constexpr int KP = KROW + 16, VP = VROW + 16;
+  // LDS rows are padded so that every lane reads at a fixed offset from its
+  // own base address without bank conflicts (64 banks x 4 bytes = 16 chunks
+  // of 16 bytes): K rows advance by 17 or 9 chunks, so the 16 consecutive rows
+  // of one MFMA-operand read land in 16 distinct chunks; 128-byte V rows
+  // advance by 10 chunks, so the two 8-row column pairs of a transposing read
+  // (chunks c and c + 1) fall on even and odd chunks respectively.
+  static constexpr int KP = KROW + 16, VP = VROW == 128 ? VROW + 32 : VROW + 16;
   static constexpr int K_BUF = kSub * KP, V_BUF = kSub * VP;
   static constexpr int LDS_BYTES = 2 * (K_BUF + V_BUF);
   static constexpr bool K_DMA = KROW == KGROW;                   // HBM -> LDS without conversion
@@ -168,8 +179,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
     return (int64_t)page * sb + (int64_t)(key & (a.page_size - 1)) * ss;
   };
-  uint8_t* const kbuf0 = smem;
-  uint8_t* const vbuf0 = smem + 2 * C::K_BUF;
+  // LDS pointers stay in the LDS address space (no generic-pointer casts).
+  lds_u8* const kbuf0 = (lds_u8*)smem;
+  lds_u8* const vbuf0 = kbuf0 + 2 * C::K_BUF;
   // Every wave issues the same number of wave-wide DMA operations per
   // sub-tile (slots past the tile repeat its last operation: identical bytes
   // to the same place), so the loop body has no per-wave branches.  Per-lane
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   auto dma_k = [&](int t, int buf) {
     if constexpr (C::K_DMA) {
       const int kv0 = t * kSub;
-      uint8_t* dst = kbuf0 + buf * C::K_BUF;
+      lds_u8* dst = kbuf0 + buf * C::K_BUF;
       if constexpr (!C::PAGED) {
         const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
 #pragma unroll
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   };
   auto dma_v = [&](int t, int buf) {
     const int kv0 = t * kSub;
-    uint8_t* dst = vbuf0 + buf * C::V_BUF;
+    lds_u8* dst = vbuf0 + buf * C::V_BUF;
     if constexpr (!C::PAGED) {
       const auto rs = tile_rsrc(vbase, a.v_ss, kv0);
 #pragma unroll
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     }
   };
   auto store_k_regs = [&](int buf) {
-    uint8_t* dst = kbuf0 + buf * C::K_BUF;
+    lds_u8* dst = kbuf0 + buf * C::K_BUF;
 #pragma unroll
     for (int i = 0; i < C::K_REG_LOADS; ++i) {
       const int id = tid + i * C::NT;
@@ -276,9 +288,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
         o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
         o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
       }
-      uint8_t* rp = dst + row * C::KP + 32 * cc;
-      *(uint4*)(rp) = make_uint4(o[0], o[1], o[2], o[3]);
-      *(uint4*)(rp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+      lds_u8* rp = dst + row * C::KP + 32 * cc;
+      *FMHA_LDS(uint4, rp) = make_uint4(o[0], o[1], o[2], o[3]);
+      *FMHA_LDS(uint4, rp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
     }
   };
 
@@ -348,9 +360,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   // S^T for one sub-tile from the K buffer `kb`.  All K operand reads are
   // issued before the first MFMA, so each MFMA waits only for its own operand
   // and the LDS latency hides behind the MFMAs ahead of it.
-  auto qk = [&](const uint8_t* kb) {
+  auto qk = [&](const lds_u8* kb, auto fence_tag) {
+    constexpr bool FENCE = decltype(fence_tag)::value;
     SAcc<C::MT> acc;
-    const uint8_t* kp = kb + kb_lane;
+    const lds_u8* kp = kb + kb_lane;
     if constexpr (C::MT == FMT_BF16 && C::PAGED) {
       // (register-lean variant for the paged path, whose address state
       // already takes more registers)
@@ -359,7 +372,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
         acc.r[T] = v16f{};
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
-          const uint4 u = *(const uint4*)(kp + 32 * T * C::KP + 16 * tt);
+          const uint4 u = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
           acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, u), q.r[tt], acc.r[T]);
         }
       }
@@ -368,8 +381,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) kr[T][tt] = *(const uint4*)(kp + 32 * T * C::KP + 16 * tt);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int tt = 0; tt < 8; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
+      if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
@@ -381,8 +394,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kr[T][i] = *(const uint4*)(kp + 32 * T * C::KP + 64 * (i >> 1) + 16 * (i & 1));
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) kr[T][i] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 64 * (i >> 1) + 16 * (i & 1));
+      if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
@@ -398,8 +411,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) kr[T][tt] = *(const uint4*)(kp + 32 * T * C::KP + 32 * tt);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int tt = 0; tt < 4; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 32 * tt);
+      if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16i{};
@@ -422,7 +435,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = v16f{};
   float m_run = -kInf;
+  // Row sums of P.  With E4M3 P they come from the matrix core: a 16x16x128
+  // product of a 0/1 matrix with the P operand (read as 128 x 16) whose row
+  // pattern selects, for the 16 queries of each lane group, the two 32-key
+  // slots that belong to that lane's query; register 0 of every lane then
+  // holds the sum for its own query.  bf16 P is summed on the VALU.
   float den = 0.0f;
+  v4f den_acc = {};
+  const v8i ones_a = (((lane >> 2) ^ (lane >> 4)) & 1) ? v8i{} : v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                                                                   0x38383838, 0x38383838, 0x38383838, 0x38383838};
   float sv_ref = 1.0f;
 
   // V-scale reference (wave-uniform).  The fast path moves the reference to
@@ -444,124 +465,161 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     v_direct = hi <= lo * 0x1p64f;
   }
 
-  // softmax + P requantisation + PV for sub-tile t from S^T `acc` and V buffer `vb`
-  auto softmax_pv = [&](const SAcc<C::MT>& acc, int t, const uint8_t* vb, auto edge_tag, auto clamp_tag,
-                        auto direct_tag) {
+  // P of one sub-tile in the PV operand format, with the V scale factor the
+  // slow V-reference path applies to its product.
+  struct PTile {
+    v8i pb;            // E4M3 P: B operand of the 32x32x64 MFMA
+    v8bf pbf[4];       // bf16 P: B operands of four 32x32x16 MFMAs
+    float f;           // product scale (slow path only)
+  };
+
+  // Softmax of one sub-tile in eight stages, so that the pipelined loop can
+  // place each next to a group of MFMAs:
+  //   0: row max, lazy decision, rescale of den (and of O off the fast path);
+  //   1-2: rescale of O, two d-tiles each (fast V-reference path);
+  //   3-6: P = 2^(s2 - m) / sp for eight keys each, clamped to the E4M3 range
+  //        only where P / sp can reach it (sfs_p given or tau above log2 448);
+  //   7: P to the PV operand format (bf16 P: also den += P).
+  struct SmState {
+    float s[32];
+    float c, negm, fo;
+    PTile pt;
+  };
+  auto sm_stage = [&](auto k_tag, SmState& st, const SAcc<C::MT>& acc, int t, auto edge_tag, auto clamp_tag,
+                      auto direct_tag) {
+    constexpr int K = decltype(k_tag)::value;
     constexpr bool EDGE = decltype(edge_tag)::value;
     constexpr bool CLAMP = decltype(clamp_tag)::value;
     constexpr bool DIRECT = decltype(direct_tag)::value;
-    const int kv0 = t * kSub;
-    // V^T operands of the four d-tiles, read before the softmax so their LDS
-    // latency hides behind it: rows 32(cq/2) + 8(cq%2) further down and
-    // columns 32d further right of the lane's base
-    // (hoisted only where registers allow it: the bf16-QK contiguous path)
-    constexpr bool HOIST_V = C::VF == FMT_E4M3 && C::MT == FMT_BF16 && !C::PAGED;
-    v8i vop[4];
-    auto read_v = [&]() {
-      const uint8_t* vp = vb + vb_lane;
+    if constexpr (K == 0) {
+      st.pt.f = 1.0f;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int e = 0; e < 32; ++e) st.s[e] = (float)acc.r[e >> 4][e & 15];
+      if constexpr (EDGE) {
+        // s[e] is key t*64 + 32(e/16) + 16g + e%16
+        const int lim = (a.causal ? min(a.Skv, qi + causal_off + 1) : a.Skv) - t * kSub;
 #pragma unroll
-        for (int cq = 0; cq < 4; ++cq) {
-          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
-          vop[d][2 * cq] = r[0];
-          vop[d][2 * cq + 1] = r[1];
+        for (int e = 0; e < 32; ++e) {
+          const int key = 32 * (e >> 4) + 16 * g + (e & 15);
+          st.s[e] = key < lim ? st.s[e] : -kInf;
         }
-    };
-    if constexpr (HOIST_V) read_v();
-    float s[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) s[e] = (float)acc.r[e >> 4][e & 15];
-    if constexpr (EDGE) {
-      // s[e] is key kv0 + 32(e/16) + 16g + e%16
-      const int lim = a.causal ? min(a.Skv, qi + causal_off + 1) : a.Skv;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int key = kv0 + 32 * (e >> 4) + 16 * g + (e & 15);
-        s[e] = key < lim ? s[e] : -kInf;
       }
-    }
-    float mx = fmaxf(s[0], s[1]);
+      float mx = fmaxf(st.s[0], st.s[1]);
 #pragma unroll
-    for (int e = 2; e < 32; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float c = C::KS ? c_q * sk_t : c_q;
-    const float tmax = mx * c;  // c > 0, so the maximum commutes with the scale
-    const bool trig = (tmax != -kInf) && (m_run == -kInf || tmax - m_run > a.tau);
-    // 2^(m - t) is 0 for an unset m (m = -inf); rows that do not trigger keep 1
-    const float e_mt = __builtin_amdgcn_exp2f(m_run - tmax);
-    const float alpha = trig ? e_mt : 1.0f;
-    m_run = trig ? tmax : m_run;
-    den *= alpha;
-    const float negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
-    // Rescale O: lazy factor and (fast path) change of V reference scale.
-    if constexpr (C::VS && DIRECT) {
-      const float fo = alpha * (sv_ref / sv_t);
-      sv_ref = sv_t;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= fo;
-    } else {
-      if (__ballot(trig) != 0) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      for (int e = 2; e < 32; e += 2) mx = fmaxf(mx, fmaxf(st.s[e], st.s[e + 1]));
+      {
+        // lanes l and l ^ 32 hold the two key halves of the same row
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-    }
-    // P = 2^(s2 - m) / sp, clamped to the E4M3 range only where P / sp can
-    // reach it (sfs_p given or tau above log2(448))
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, negm));
-      if constexpr (CLAMP) s[e] = fminf(s[e], 448.0f);
-    }
-    if constexpr (C::VF == FMT_E4M3) {
-      v8i pb;
-      float dsum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        int pk = pack_e4m3<false>(s[4 * w], s[4 * w + 1], 0);
-        pk = pack_e4m3<true>(s[4 * w + 2], s[4 * w + 3], pk);
-        pb[w] = pk;
-        const v2f lo = unpack_e4m3<false>(pk);
-        const v2f hi = unpack_e4m3<true>(pk);
-        dsum += (lo.x + lo.y) + (hi.x + hi.y);
-      }
-      den += dsum;
-      if constexpr (!HOIST_V) read_v();
-      if constexpr (!C::VS || DIRECT) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = mfma_f8(vop[d], pb, o[d]);
+      st.c = C::KS ? c_q * sk_t : c_q;
+      const float tmax = mx * st.c;  // c > 0, so the maximum commutes with the scale
+      const bool trig = (tmax != -kInf) & ((m_run == -kInf) | (tmax - m_run > a.tau));  // no short-circuit branches
+      // 2^(m - t) is 0 for an unset m (m = -inf); rows that do not trigger keep 1
+      const float e_mt = __builtin_amdgcn_exp2f(m_run - tmax);
+      const float alpha = trig ? e_mt : 1.0f;
+      m_run = trig ? tmax : m_run;
+      if constexpr (C::VF == FMT_E4M3) den_acc[0] *= alpha;
+      else den *= alpha;
+      st.negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
+      if constexpr (C::VS && DIRECT) {
+        // one factor folds the lazy rescale and the change of V reference
+        st.fo = alpha * (sv_ref * __builtin_amdgcn_rcpf(sv_t));
+        sv_ref = sv_t;
       } else {
-        const float f = sv_t / sv_ref;  // reference stays at 1
+        if (__ballot(trig) != 0) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const v16f part = mfma_f8(vop[d], pb, v16f{});
+          for (int d = 0; d < 4; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], f, o[d][r]);
+            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
         }
+        if constexpr (C::VS) st.pt.f = sv_t / sv_ref;  // reference stays at 1
       }
+    } else if constexpr (K == 1 || K == 2) {
+      if constexpr (C::VS && DIRECT) {
+#pragma unroll
+        for (int d = 2 * (K - 1); d < 2 * K; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= st.fo;
+      }
+    } else if constexpr (K >= 3 && K <= 6) {
+#pragma unroll
+      for (int e = 8 * (K - 3); e < 8 * (K - 2); ++e) {
+        st.s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[e], st.c, st.negm));
+        if constexpr (CLAMP) st.s[e] = fminf(st.s[e], 448.0f);
+      }
+    } else {
+      if constexpr (C::VF == FMT_E4M3) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          int pk = pack_e4m3<false>(st.s[4 * w], st.s[4 * w + 1], 0);
+          pk = pack_e4m3<true>(st.s[4 * w + 2], st.s[4 * w + 3], pk);
+          st.pt.pb[w] = pk;
+        }
+      } else {
+        float dsum = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = f32_to_bf16_bits(st.s[8 * kk + 2 * j]);
+            const uint32_t hi = f32_to_bf16_bits(st.s[8 * kk + 2 * j + 1]);
+            w[j] = lo | (hi << 16);
+            dsum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+          }
+          st.pt.pbf[kk] = __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        den += dsum;
+      }
+    }
+  };
+  // The whole softmax of sub-tile t: P and the slow-path product scale.
+  auto softmax_p = [&](const SAcc<C::MT>& acc, int t, auto edge_tag, auto clamp_tag, auto direct_tag) {
+    SmState st;
+    static_for<0, 8>([&](auto k) { sm_stage(k, st, acc, t, edge_tag, clamp_tag, direct_tag); });
+    return st.pt;
+  };
+
+  // V^T operand (E4M3 V) of d-tile d from V buffer `vb`: rows 32(cq/2) +
+  // 8(cq%2) further down and columns 32d further right of the lane's base.
+  auto read_vop = [&](const lds_u8* vb, int d) {
+    v8i v;
+    const lds_u8* vp = vb + vb_lane;
+#pragma unroll
+    for (int cq = 0; cq < 4; ++cq) {
+      const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          FMHA_LDS(v2i, vp + (32 * (cq >> 1) + 8 * (cq & 1)) * C::VP + 32 * d));
+      v[2 * cq] = r[0];
+      v[2 * cq + 1] = r[1];
+    }
+    return v;
+  };
+  // O^T += V^T P^T for one sub-tile from V buffer `vb`; with E4M3 P the row
+  // sums of P come from the same operand.
+  auto pv_e4m3 = [&](const PTile& pt, const v8i* vop, auto direct_tag) {
+    constexpr bool DIRECT = decltype(direct_tag)::value;
+    den_acc = mfma_f8_16(ones_a, pt.pb, den_acc);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if constexpr (!C::VS || DIRECT) {
+        o[d] = mfma_f8(vop[d], pt.pb, o[d]);
+      } else {
+        const v16f part = mfma_f8(vop[d], pt.pb, v16f{});
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(part[r], pt.f, o[d][r]);
+      }
+    }
+  };
+  auto pv = [&](const PTile& pt, const lds_u8* vb, auto direct_tag) {
+    const lds_u8* vp = vb + vb_lane;
+    if constexpr (C::VF == FMT_E4M3) {
+      v8i vop[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vb, d);
+      pv_e4m3(pt, vop, direct_tag);
     } else {
       // bf16 P and V (V unscaled).
-      v8bf pbf[4];
-      float dsum = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = f32_to_bf16_bits(s[8 * kk + 2 * j]);
-          const uint32_t hi = f32_to_bf16_bits(s[8 * kk + 2 * j + 1]);
-          w[j] = lo | (hi << 16);
-          dsum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
-        }
-        pbf[kk] = __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-      den += dsum;
-      const uint8_t* vp = vb + vb_lane;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -575,17 +633,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
             w[2 * cq] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
             w[2 * cq + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
           }
-          o[d] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), pbf[kk], o[d]);
+          o[d] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), pt.pbf[kk], o[d]);
         }
       }
     }
   };
 
+
   // ---- main loop over 64-key sub-tiles, K/V double-buffered in LDS.  Per
   // sub-tile a wave runs S^T = K Q^T (MFMA), the softmax (VALU), then
-  // O^T += V^T P^T (MFMA); an MFMA holds its wave's issue for its whole
-  // duration on this hardware, so MFMA/VALU overlap comes from the second
-  // wave on the SIMD (another workgroup) being in the opposite phase.
+  // O^T += V^T P^T (MFMA); MFMA/VALU overlap comes from the other wave on the
+  // SIMD being in another phase.  The copies of the next sub-tile are issued
+  // first and land while the current one is processed.
   int tc = next_sub(0);
   if (tc < n_sub) {
     dma_k(tc, 0);
@@ -595,7 +654,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
       store_k_regs(0);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
   int buf = 0;
   auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
@@ -606,12 +665,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
       dma_v(tn, buf ^ 1);
       if constexpr (!C::K_DMA) load_k_regs(tn);
     }
-    const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF);
-    softmax_pv(acc, tc, vbuf0 + buf * C::V_BUF, edge_tag, clamp_tag, direct_tag);
+    const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
+    pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
     if constexpr (!C::K_DMA) {
       if (tn < n_sub) store_k_regs(buf ^ 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
     buf ^= 1;
     tc = tn;
@@ -638,7 +697,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   }
 
   // ---- epilogue: O = num / den in bf16; rows without a valid key give 0
-  const float dt = den + __shfl_xor(den, 32, 64);
+  float dt;
+  if constexpr (C::VF == FMT_E4M3) dt = den_acc[0];
+  else dt = den + __shfl_xor(den, 32, 64);
   const float inv = dt > 0.0f ? sv_ref / dt : 0.0f;
   if (qi >= a.Sq) return;
   uint8_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)qi * a.o_ss;
@@ -663,7 +724,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles);
-  const size_t lds = (size_t)C::LDS_BYTES;
+  const size_t lds = (size_t)C::LDS_BYTES + 64;  // + wave -> SIMD table
   static bool configured = false;  // benign race: the attribute is idempotent
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -12,12 +12,14 @@ typedef __attribute__((ext_vector_type(4))) int v4i;
 typedef __attribute__((ext_vector_type(8))) int v8i;
 typedef __attribute__((ext_vector_type(16))) int v16i;
 typedef __attribute__((ext_vector_type(2))) float v2f;
+typedef __attribute__((ext_vector_type(4))) float v4f;
 typedef __attribute__((ext_vector_type(16))) float v16f;
 typedef __attribute__((ext_vector_type(8))) __bf16 v8bf;
 typedef __attribute__((ext_vector_type(4))) short v4s;
 typedef __attribute__((ext_vector_type(2))) unsigned short v2us;
 
 #define FMHA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) uint8_t lds_u8;  // byte in LDS
 
 // ---------------------------------------------------------------- MFMA
 // 32x32 output tiles.  Operand layout (checked on gfx950): lane l supplies row
@@ -32,6 +34,13 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
 // E4M3 x E4M3 with unit block scales (E8M0 exponent 127 = 2^0).
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x128 E4M3 product: lane l supplies row (A) / column (B) l % 16 and
+// contraction slots 32*(l/16) .. +32 (byte i of the 8 registers = slot +i);
+// result register r of lane l is row 4*(l/16) + r, column l % 16.
+__device__ __forceinline__ v4f mfma_f8_16(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // ---------------------------------------------------------------- formats
