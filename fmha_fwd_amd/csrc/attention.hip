@@ -69,9 +69,11 @@ struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
   static constexpr int MT = QF;                                  // QK operand format
-  static constexpr int KROW = MT == FMT_BF16 ? 256 : 128;        // bytes per K row (LDS format)
+  // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
+  // as each MFMA operand is read.
+  static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
+  static constexpr int KROW = KF == FMT_BF16 ? 256 : 128;        // bytes per K row (HBM and LDS)
   static constexpr int VROW = VF == FMT_BF16 ? 256 : 128;
-  static constexpr int KGROW = KF == FMT_BF16 ? 256 : 128;       // bytes per K row in HBM
   // LDS rows are padded so that every lane reads at a fixed offset from its
   // own base address without bank conflicts (64 banks x 4 bytes = 16 chunks
   // of 16 bytes): K rows advance by 17 or 9 chunks, so the 16 consecutive rows
@@ -81,16 +83,12 @@ struct Cfg {
   static constexpr int KP = KROW + 16, VP = VROW == 128 ? VROW + 32 : VROW + 16;
   static constexpr int K_BUF = kSub * KP, V_BUF = kSub * VP;
   static constexpr int LDS_BYTES = 2 * (K_BUF + V_BUF);
-  static constexpr bool K_DMA = KROW == KGROW;                   // HBM -> LDS without conversion
   static constexpr int NT = NW * 64;
   static constexpr int K_CPR = KROW / 16, KP_CPR = KP / 16;      // 16-byte chunks per row
   static constexpr int V_CPR = VROW / 16, VP_CPR = VP / 16;
   static constexpr int K_DMA_OPS = K_BUF / 1024;                 // 1 KB per wave-wide DMA
   static constexpr int V_DMA_OPS = V_BUF / 1024;
   static_assert(K_BUF % 1024 == 0 && V_BUF % 1024 == 0, "DMA granularity");
-  static constexpr int KG_CPR = KGROW / 16;                      // register path (widening K)
-  static constexpr int K_REG_LOADS = K_DMA ? 0 : kSub * KG_CPR / NT;
-  static_assert(K_DMA || kSub * KG_CPR % NT == 0, "tile / thread mismatch");
   static_assert(!(KF == FMT_E4M3 && QF == FMT_INT8), "unsupported");
   static_assert(QF == KF || (QF == FMT_BF16 && KF == FMT_E4M3), "unsupported");
 };
@@ -189,10 +187,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   // buffer resource whose range ends at the last token, so rows past the end
   // of the sequence read as zeros.  K rows are stored in MFMA row order: LDS
   // row 32T + m holds key 32T + sigma(m).
-  constexpr int KSL = C::K_DMA ? (C::K_DMA_OPS + C::NW - 1) / C::NW : 0;
+  constexpr int KSL = (C::K_DMA_OPS + C::NW - 1) / C::NW;
   constexpr int VSL = (C::V_DMA_OPS + C::NW - 1) / C::NW;
-  uint32_t k_src[KSL > 0 ? KSL : 1], v_src[VSL];
-  int k_row[KSL > 0 ? KSL : 1], v_row[VSL];  // key within the tile (paged path)
+  uint32_t k_src[KSL], v_src[VSL];
+  int k_row[KSL], v_row[VSL];  // key within the tile (paged path)
 #pragma unroll
   for (int sl = 0; sl < KSL; ++sl) {
     const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
@@ -221,23 +219,21 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * ss), 0, nrec, 0x00020000);
   };
   auto dma_k = [&](int t, int buf) {
-    if constexpr (C::K_DMA) {
-      const int kv0 = t * kSub;
-      lds_u8* dst = kbuf0 + buf * C::K_BUF;
-      if constexpr (!C::PAGED) {
-        const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
+    const int kv0 = t * kSub;
+    lds_u8* dst = kbuf0 + buf * C::K_BUF;
+    if constexpr (!C::PAGED) {
+      const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
 #pragma unroll
-        for (int sl = 0; sl < KSL; ++sl) {
-          const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
-        }
-      } else {
+      for (int sl = 0; sl < KSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int sl = 0; sl < KSL; ++sl) {
-          const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
-          const uint8_t* src = kbase + token_off(kv0 + k_row[sl], a.k_sb, a.k_ss) + k_src[sl];
-          __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
-        }
+      for (int sl = 0; sl < KSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+        const uint8_t* src = kbase + token_off(kv0 + k_row[sl], a.k_sb, a.k_ss) + k_src[sl];
+        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }
   };
@@ -260,40 +256,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
       }
     }
   };
-  // Register path for K when its LDS format differs (E4M3 widened to bf16).
-  uint4 kreg[C::K_REG_LOADS > 0 ? C::K_REG_LOADS : 1];
-  auto load_k_regs = [&](int t) {
-    const int kv0 = t * kSub;
-#pragma unroll
-    for (int i = 0; i < C::K_REG_LOADS; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::KG_CPR, cc = id % C::KG_CPR;
-      const int key = kv0 + 32 * (row >> 5) + sigma(row & 31);
-      kreg[i] = *(const uint4*)(kbase + token_off(key, a.k_sb, a.k_ss) + cc * 16);
-    }
-  };
-  auto store_k_regs = [&](int buf) {
-    lds_u8* dst = kbuf0 + buf * C::K_BUF;
-#pragma unroll
-    for (int i = 0; i < C::K_REG_LOADS; ++i) {
-      const int id = tid + i * C::NT;
-      const int row = id / C::KG_CPR, cc = id % C::KG_CPR;
-      // E4M3 codes widened to bf16 (exact: 4 significant bits).
-      uint32_t w[4] = {kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v2f lo = unpack_e4m3<false>((int)w[j]);
-        v2f hi = unpack_e4m3<true>((int)w[j]);
-        o[2 * j] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-        o[2 * j + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-      }
-      lds_u8* rp = dst + row * C::KP + 32 * cc;
-      *FMHA_LDS(uint4, rp) = make_uint4(o[0], o[1], o[2], o[3]);
-      *FMHA_LDS(uint4, rp + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-  };
-
   // ---- Q tile into registers (B operand of S^T = K Q^T)
   QRegs<C::MT> q;
   {
@@ -347,7 +309,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   // ---- per-lane LDS read bases (stage-relative; every operand read is a
   //      fixed immediate offset from these)
   int kb_lane;
-  if constexpr (C::MT == FMT_BF16) kb_lane = m32 * C::KP + 128 * g;
+  if constexpr (C::WIDEN) kb_lane = m32 * C::KP + 64 * g;
+  else if constexpr (C::MT == FMT_BF16) kb_lane = m32 * C::KP + 128 * g;
   else if constexpr (C::MT == FMT_E4M3) kb_lane = m32 * C::KP + 32 * g;
   else kb_lane = m32 * C::KP + 16 * g;
   const int tr_G = lane >> 4;
@@ -364,16 +327,22 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     constexpr bool FENCE = decltype(fence_tag)::value;
     SAcc<C::MT> acc;
     const lds_u8* kp = kb + kb_lane;
-    if constexpr (C::MT == FMT_BF16 && C::PAGED) {
-      // (register-lean variant for the paged path, whose address state
-      // already takes more registers)
+    if constexpr (C::WIDEN) {
+      // E4M3 K: one 16-byte read holds the operands of two MFMAs (d =
+      // 64g + 16j .. +16), widened to bf16 just before use
+      uint4 kr[2][4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[T][j] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * j);
+      if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const uint4 u = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
-          acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, u), q.r[tt], acc.r[T]);
+        for (int j = 0; j < 4; ++j) {
+          acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].x, kr[T][j].y), q.r[2 * j], acc.r[T]);
+          acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].z, kr[T][j].w), q.r[2 * j + 1], acc.r[T]);
         }
       }
     } else if constexpr (C::MT == FMT_BF16) {
@@ -649,10 +618,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   if (tc < n_sub) {
     dma_k(tc, 0);
     dma_v(tc, 0);
-    if constexpr (!C::K_DMA) {
-      load_k_regs(tc);
-      store_k_regs(0);
-    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
@@ -663,23 +628,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     if (tn < n_sub) {
       dma_k(tn, buf ^ 1);
       dma_v(tn, buf ^ 1);
-      if constexpr (!C::K_DMA) load_k_regs(tn);
     }
     const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
     pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
-    if constexpr (!C::K_DMA) {
-      if (tn < n_sub) store_k_regs(buf ^ 1);
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
     buf ^= 1;
     tc = tn;
   };
   auto run = [&](auto clamp_tag, auto direct_tag) {
-    // sub-tiles valid for every pair of the workgroup first, then the edge ones
-    if constexpr (!C::MASKED) {
-      while (tc < n_sub && tc < full_end) step(std::false_type{}, clamp_tag, direct_tag);
-    }
+    // sub-tiles valid for every pair of the workgroup first (a block mask
+    // only skips whole sub-tiles), then the edge ones
+    while (tc < n_sub && tc < full_end) step(std::false_type{}, clamp_tag, direct_tag);
     while (tc < n_sub) step(std::true_type{}, clamp_tag, direct_tag);
   };
   const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;

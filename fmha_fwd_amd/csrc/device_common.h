@@ -55,6 +55,16 @@ template <bool HI>
 __device__ __forceinline__ v2f unpack_e4m3(int packed) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(packed, HI);
 }
+// Eight E4M3 codes (byte i of w0:w1 = element i) -> eight bf16, exactly
+// (every E4M3 value, subnormals included, is a bf16 value).
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 v2bf;
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
