@@ -147,7 +147,8 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   }
   if (paged) {
     const int ps = p->page_size;
-    if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1))) return fail(FMHA_ERR_UNSUPPORTED, "fwd: page_size=%d (a power of two)", ps);
+    if (ps < 16 || ps > (1 << 20) || (ps & (ps - 1)))
+      return fail(FMHA_ERR_UNSUPPORTED, "fwd: page_size=%d (a power of two, at least 16)", ps);
     if (p->num_pages < 1) return fail(FMHA_ERR_INVALID, "fwd: num_pages=%d", p->num_pages);
     if (p->page_table_stride_b < 0) return fail(FMHA_ERR_INVALID, "fwd: negative page_table_stride_b");
   }

@@ -167,16 +167,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     vbase += (int64_t)b * a.v_sb;
   }
   const int page_shift = C::PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
-  // Byte offset of token `key`, clamped into the sequence (rows past the end
-  // load the last token, whose pairs are masked); a page-table entry outside
-  // the pool reads page 0.
-  auto token_off = [&](int key, const int64_t sb, const int64_t ss) -> int64_t {
-    key = min(key, a.Skv - 1);
-    if (!C::PAGED) return (int64_t)key * ss;
-    int page = pt_row[key >> page_shift];
-    page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
-    return (int64_t)page * sb + (int64_t)(key & (a.page_size - 1)) * ss;
-  };
   // LDS pointers stay in the LDS address space (no generic-pointer casts).
   lds_u8* const kbuf0 = (lds_u8*)smem;
   lds_u8* const vbuf0 = kbuf0 + 2 * C::K_BUF;
@@ -187,38 +177,84 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   // buffer resource whose range ends at the last token, so rows past the end
   // of the sequence read as zeros.  K rows are stored in MFMA row order: LDS
   // row 32T + m holds key 32T + sigma(m).
+  //
+  // Paged K/V (pages of 16 tokens or more, so at most four per sub-tile):
+  // the page numbers of a sub-tile are read once, one table entry per lane
+  // and a sub-tile ahead; each copy then takes its page from the lane that
+  // holds it (ds_bpermute).  Every lane keeps, per slot, its page slot within
+  // the sub-tile (2 bits) and its byte offset inside the page.  In the
+  // sub-tile that crosses the end of the sequence, rows past the end read
+  // the last token instead.
   constexpr int KSL = (C::K_DMA_OPS + C::NW - 1) / C::NW;
   constexpr int VSL = (C::V_DMA_OPS + C::NW - 1) / C::NW;
-  uint32_t k_src[KSL], v_src[VSL];
-  int k_row[KSL], v_row[VSL];  // key within the tile (paged path)
-#pragma unroll
-  for (int sl = 0; sl < KSL; ++sl) {
-    const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+  static_assert(2 * (KSL + VSL) <= 64, "page-slot bits");
+  uint32_t k_src[KSL], v_src[VSL];  // contiguous: byte offset in the tile; paged: in the page
+  uint64_t pslot_bits = 0;          // paged: 2-bit page slot of every K and V slot
+  const int tshift = min(page_shift, 6);  // rows of one sub-tile per page: 1 << tshift
+  const int tmask = (1 << tshift) - 1;
+  // Row of the sub-tile (a key offset) and byte column of this lane in copy j.
+  auto k_copy_row = [&](int j, int& ch) {
     const int cid = j * 64 + lane;
     const int row = cid / C::KP_CPR;
-    int ch = cid % C::KP_CPR;
+    ch = cid % C::KP_CPR;
     ch = ch < C::K_CPR ? ch : 0;  // the pad chunk: any valid bytes
-    k_row[sl] = 32 * (row >> 5) + sigma(row & 31);
-    k_src[sl] = (uint32_t)(k_row[sl] * a.k_ss) + ch * 16;
-    if (C::PAGED) k_src[sl] = ch * 16;
+    return 32 * (row >> 5) + sigma(row & 31);
+  };
+  auto v_copy_row = [&](int j, int& ch) {
+    const int cid = j * 64 + lane;
+    ch = cid % C::VP_CPR;
+    ch = ch < C::V_CPR ? ch : 0;
+    return cid / C::VP_CPR;
+  };
+#pragma unroll
+  for (int sl = 0; sl < KSL; ++sl) {
+    int ch;
+    const int row = k_copy_row(min(wave + sl * C::NW, C::K_DMA_OPS - 1), ch);
+    if (!C::PAGED) {
+      k_src[sl] = (uint32_t)(row * a.k_ss) + ch * 16;
+    } else {
+      k_src[sl] = (uint32_t)((row & tmask) * a.k_ss) + ch * 16;
+      pslot_bits |= (uint64_t)(row >> tshift) << (2 * sl);
+    }
   }
 #pragma unroll
   for (int sl = 0; sl < VSL; ++sl) {
-    const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
-    const int cid = j * 64 + lane;
-    const int row = cid / C::VP_CPR;
-    int ch = cid % C::VP_CPR;
-    ch = ch < C::V_CPR ? ch : 0;
-    v_row[sl] = row;
-    v_src[sl] = (uint32_t)(row * a.v_ss) + ch * 16;
-    if (C::PAGED) v_src[sl] = ch * 16;
+    int ch;
+    const int row = v_copy_row(min(wave + sl * C::NW, C::V_DMA_OPS - 1), ch);
+    if (!C::PAGED) {
+      v_src[sl] = (uint32_t)(row * a.v_ss) + ch * 16;
+    } else {
+      v_src[sl] = (uint32_t)((row & tmask) * a.v_ss) + ch * 16;
+      pslot_bits |= (uint64_t)(row >> tshift) << (2 * (KSL + sl));
+    }
   }
+  // Page numbers of sub-tile t: entry i of the sub-tile in lane i (i < 4).
+  auto load_pages = [&](int t) {
+    if constexpr (!C::PAGED) return 0;
+    const int first = (t * kSub) >> page_shift, last = (a.Skv - 1) >> page_shift;
+    int page = pt_row[min(first + (lane & 3), last)];
+    return (unsigned)page < (unsigned)a.num_pages ? page : 0;  // outside the pool: page 0
+  };
   auto tile_rsrc = [&](const uint8_t* base, int64_t ss, int kv0) {
     const uint64_t rem = (uint64_t)(a.Skv - kv0) * (uint64_t)ss;
     const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * ss), 0, nrec, 0x00020000);
   };
-  auto dma_k = [&](int t, int buf) {
+  // Source of one paged copy (slot bit field `idx`, in-page offset `off`).
+  // In the last sub-tile a row past the end takes the last token's page slot
+  // and offset (row `rl` of the sub-tile).
+  auto paged_src = [&](const uint8_t* base, int64_t sb, int64_t ss, int kv0, int pages, int idx, uint32_t off,
+                       bool past_end, int rl, int ch) {
+    int ps = (int)(pslot_bits >> (2 * idx)) & 3;
+    if (past_end) {
+      ps = rl >> tshift;
+      off = (uint32_t)((rl & tmask) * ss) + ch * 16;
+    }
+    const int page = __builtin_amdgcn_ds_bpermute(ps << 2, pages);
+    const int64_t in_page = (int64_t)(kv0 & (a.page_size - 1)) * ss;  // pages longer than a sub-tile
+    return base + (int64_t)page * sb + in_page + off;
+  };
+  auto dma_k = [&](int t, int buf, int pages) {
     const int kv0 = t * kSub;
     lds_u8* dst = kbuf0 + buf * C::K_BUF;
     if constexpr (!C::PAGED) {
@@ -228,16 +264,26 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
         const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
       }
-    } else {
+    } else if (kv0 + kSub <= a.Skv) {
 #pragma unroll
       for (int sl = 0; sl < KSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
-        const uint8_t* src = kbase + token_off(kv0 + k_row[sl], a.k_sb, a.k_ss) + k_src[sl];
+        const uint8_t* src = paged_src(kbase, a.k_sb, a.k_ss, kv0, pages, sl, k_src[sl], false, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+      }
+    } else {
+      const int rl = a.Skv - 1 - kv0;
+#pragma unroll
+      for (int sl = 0; sl < KSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+        int ch;
+        const int row = k_copy_row(j, ch);
+        const uint8_t* src = paged_src(kbase, a.k_sb, a.k_ss, kv0, pages, sl, k_src[sl], row > rl, rl, ch);
         __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }
   };
-  auto dma_v = [&](int t, int buf) {
+  auto dma_v = [&](int t, int buf, int pages) {
     const int kv0 = t * kSub;
     lds_u8* dst = vbuf0 + buf * C::V_BUF;
     if constexpr (!C::PAGED) {
@@ -247,11 +293,21 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
         const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], 0, 0, 0);
       }
-    } else {
+    } else if (kv0 + kSub <= a.Skv) {
 #pragma unroll
       for (int sl = 0; sl < VSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
-        const uint8_t* src = vbase + token_off(kv0 + v_row[sl], a.v_sb, a.v_ss) + v_src[sl];
+        const uint8_t* src = paged_src(vbase, a.v_sb, a.v_ss, kv0, pages, KSL + sl, v_src[sl], false, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+      }
+    } else {
+      const int rl = a.Skv - 1 - kv0;
+#pragma unroll
+      for (int sl = 0; sl < VSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
+        int ch;
+        const int row = v_copy_row(j, ch);
+        const uint8_t* src = paged_src(vbase, a.v_sb, a.v_ss, kv0, pages, KSL + sl, v_src[sl], row > rl, rl, ch);
         __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }
@@ -613,21 +669,28 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
   // sub-tile a wave runs S^T = K Q^T (MFMA), the softmax (VALU), then
   // O^T += V^T P^T (MFMA); MFMA/VALU overlap comes from the other wave on the
   // SIMD being in another phase.  The copies of the next sub-tile are issued
-  // first and land while the current one is processed.
+  // first and land while the current one is processed (paged: its page
+  // numbers were read during the previous sub-tile).
   int tc = next_sub(0);
+  int tn = n_sub, pg_n = 0;
   if (tc < n_sub) {
-    dma_k(tc, 0);
-    dma_v(tc, 0);
+    const int pg_c = load_pages(tc);
+    dma_k(tc, 0, pg_c);
+    dma_v(tc, 0, pg_c);
+    tn = next_sub(tc + 1);
+    if (tn < n_sub) pg_n = load_pages(tn);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
   int buf = 0;
   auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
     fetch_scales(tc);
-    const int tn = next_sub(tc + 1);
+    int tnn = n_sub;
     if (tn < n_sub) {
-      dma_k(tn, buf ^ 1);
-      dma_v(tn, buf ^ 1);
+      dma_k(tn, buf ^ 1, pg_n);
+      dma_v(tn, buf ^ 1, pg_n);
+      tnn = next_sub(tn + 1);
+      if (C::PAGED && tnn < n_sub) pg_n = load_pages(tnn);
     }
     const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
     pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
@@ -635,6 +698,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVE
     __syncthreads();
     buf ^= 1;
     tc = tn;
+    tn = tnn;
   };
   auto run = [&](auto clamp_tag, auto direct_tag) {
     // sub-tiles valid for every pair of the workgroup first (a block mask

@@ -145,4 +145,5 @@ def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
     """A reduced-size variant of a configuration (same formats and options)."""
     s = SPECS[base]
     return Spec(s.name + f"_S{S}", s.index, B or s.B, Hq or s.Hq, Hkv or s.Hkv, S, s.q_fmt, s.k_fmt, s.v_fmt,
-                kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged), s.page_size)
+                kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged),
+                kw.get("page_size", s.page_size))

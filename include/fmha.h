@@ -141,12 +141,12 @@ typedef struct {
   int32_t mask_block_q, mask_block_kv;   /* 64, 256 */
   /* Paged K/V: int32 [B, ceil(Skv / page_size)] with row stride
    * page_table_stride_b; entry p of row b is the pool page holding logical
-   * tokens [p * page_size, (p + 1) * page_size).  Entries outside
-   * [0, num_pages) make the tokens of that page invalid (never read).
-   * NULL = contiguous K/V. */
+   * tokens [p * page_size, (p + 1) * page_size).  An entry outside
+   * [0, num_pages) is read as page 0 (no access outside the pool; the
+   * output for such tokens is unspecified).  NULL = contiguous K/V. */
   const int32_t* page_table;
   int64_t page_table_stride_b;
-  int32_t page_size;         /* 16 */
+  int32_t page_size;         /* tokens per page: a power of two >= 16 (16 in the block-sparse workload) */
   int32_t num_pages;
 } fmha_fwd_params;
 

@@ -109,6 +109,7 @@ def _call(lib, p):
     (dict(block_mask=FAKE, mask_block_q=128, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "mask_block_q"),
     (dict(block_mask=FAKE, mask_block_q=64, mask_block_kv=100), F.FMHA_ERR_UNSUPPORTED, "mask_block_kv"),
     (dict(page_table=FAKE, page_size=12, num_pages=4), F.FMHA_ERR_UNSUPPORTED, "page_size"),
+    (dict(page_table=FAKE, page_size=8, num_pages=4), F.FMHA_ERR_UNSUPPORTED, "page_size"),
     (dict(page_table=FAKE, page_size=16, num_pages=0), F.FMHA_ERR_INVALID, "num_pages"),
     (dict(sfs_p=FAKE + 2), F.FMHA_ERR_INVALID, "sfs_p"),
 ])

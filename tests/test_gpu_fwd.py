@@ -60,6 +60,13 @@ def test_small_paged_dense():
     _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=1, masked=False))
 
 
+@pytest.mark.parametrize("page_size", [32, 64, 128, 256])
+@pytest.mark.parametrize("masked", [False, True])
+def test_small_paged_page_sizes(page_size, masked):
+    # pages of 16..64 tokens split a 64-key sub-tile; longer ones hold several
+    _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=2, masked=masked, page_size=page_size))
+
+
 def test_sfs_p_and_tau_variants():
     spec = W.small_spec("gqa", 320, B=1, Hq=4, Hkv=2)
     sp = torch.tensor([1.0, 0.25, 0.1, 2.0], dtype=torch.float32, device="cuda")
