@@ -44,8 +44,14 @@ constexpr int kSub = 64;  // keys per sub-tile: lazy-decision and V-scale unit
 #define FMHA_DENSE_WAVES 4
 #endif
 constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per dense workgroup
-#ifndef FMHA_WAVES_PER_EU
-#define FMHA_WAVES_PER_EU 2  // register budget: 512 / 2 VGPRs per lane
+// Wavefronts per SIMD the register budget is cut for (512 / n VGPRs per
+// lane): three where the loop fits 168 registers (E4M3 or int8 QK, whose Q
+// operand takes 16 registers), two otherwise.
+#ifndef FMHA_WAVES_PER_EU_8BIT
+#define FMHA_WAVES_PER_EU_8BIT 3
+#endif
+#ifndef FMHA_WAVES_PER_EU_BF16
+#define FMHA_WAVES_PER_EU_BF16 2
 #endif
 constexpr float kInf = __builtin_huge_valf();
 
@@ -69,6 +75,7 @@ struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
   static constexpr int MT = QF;                                  // QK operand format
+  static constexpr int WPE = MT == FMT_BF16 || MASKED || PAGED ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
@@ -113,7 +120,7 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(FMHA_WAVES_PER_EU))) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE))) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
