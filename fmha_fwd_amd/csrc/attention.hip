@@ -536,9 +536,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
           st.s[e] = key < lim ? st.s[e] : -kInf;
         }
       }
-      float mx = fmaxf(st.s[0], st.s[1]);
+      // 3-input max tree: 32 -> 11 -> 4 -> 1 (16 v_max3)
+      float m1[11];
 #pragma unroll
-      for (int e = 2; e < 32; e += 2) mx = fmaxf(mx, fmaxf(st.s[e], st.s[e + 1]));
+      for (int i = 0; i < 10; ++i) m1[i] = fmaxf(fmaxf(st.s[3 * i], st.s[3 * i + 1]), st.s[3 * i + 2]);
+      m1[10] = fmaxf(st.s[30], st.s[31]);
+      const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+      const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
+      float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
       {
         // lanes l and l ^ 32 hold the two key halves of the same row
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -700,7 +705,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       if (C::PAGED && tnn < n_sub) pg_n = load_pages(tnn);
     }
     const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
-    pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
+    if constexpr (C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED) {
+      // V operands are read before the softmax so their LDS latency hides
+      // behind it (32 more live registers: two-wave dense instances only)
+      v8i vop[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + buf * C::V_BUF, d);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_e4m3(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vop, direct_tag);
+    } else {
+      pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
     buf ^= 1;
