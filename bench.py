@@ -211,6 +211,7 @@ def main():
     f_ms = [e[1].elapsed_time(e[2]) for e in events]
     ms_step = wall * 1e3 / args.steps
     fwd_ms = float(np.mean(f_ms))
+    fwd_median, fwd_min = float(np.median(f_ms)), float(np.min(f_ms))
 
     pairs = pair_count(spec, data)
     flops = 4.0 * spec.D * pairs
@@ -220,12 +221,13 @@ def main():
     achieved = flops / (fwd_ms * 1e-3) / 1e12
     quant_bytes = sum(x.numel() * 3 + s.numel() * 4 for _, x, _, _, s in quant)
 
-    traffic = None
+    traffic, sclk = None, None
     tfile = os.path.join(ROOT, "profiles", f"fwd_{spec.name}_traffic.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("source_hash") == source_hash():
             traffic = t.get("bytes_per_launch")
+            sclk = t.get("sclk_ghz")
 
     rec = {
         "metric": METRIC,
@@ -246,8 +248,15 @@ def main():
                    "unmasked_pairs": pairs, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "fmha_fwd", "frac_of_fp8_peak": achieved / PEAK["e4m3"]},
+                     "kernel": "fmha_fwd", "frac_of_fp8_peak": achieved / PEAK["e4m3"],
+                     # shader clock measured under this kernel (counters), and the fraction of
+                     # the peak at that clock (the published peaks assume 2.4 GHz)
+                     "sclk_ghz_measured": sclk,
+                     "frac_at_measured_sclk": None if sclk is None else achieved / (peak * sclk / 2.4)},
         "fwd_ms": fwd_ms,
+        "fwd_ms_median": fwd_median,
+        "fwd_ms_min": fwd_min,
+        "fwd_tflops_at_min": flops / (fwd_min * 1e-3) / 1e12,
         "quantize_ms": float(np.mean(q_ms)) if quant else 0.0,
         "quantize_gbs": (quant_bytes / (np.mean(q_ms) * 1e-3) / 1e9) if quant else None,
     }
