@@ -82,15 +82,16 @@ def cpu_baseline(spec, data, budget_s=12.0):
     rows_done, pairs_done, t_att = 0, 0, 0.0
     bm = data.get("block_mask")
     bm = None if bm is None else bm[:1, [h]]
-    while t_att < budget_s and rows_done < spec.S:
-        rows = np.sort(rng.choice(spec.S, size=min(64, spec.S), replace=False))
+    nq = spec.n_q
+    while t_att < budget_s and rows_done < nq:
+        rows = np.sort(rng.choice(nq, size=min(64, nq), replace=False))
         t0 = time.perf_counter()
         attention(qd, kd, vd, causal=spec.causal, block_mask=bm, mode="lazy",
                   p_format=spec.v_fmt, rows=rows, heads=[(0, 0)])
         t_att += time.perf_counter() - t0
         rows_done += len(rows)
         if spec.causal:
-            pairs_done += int(np.minimum(rows + 1, spec.S).sum())
+            pairs_done += int(np.minimum(rows + spec.S - nq + 1, spec.S).sum())
         elif bm is not None:
             pairs_done += int(sum(bm[0, 0, r // 64].sum() * 256 for r in rows))
         else:
@@ -184,7 +185,7 @@ def main():
             pool[pt.reshape(-1).long()] = c.reshape(spec.B * per_seq, ps, spec.Hkv, spec.D)
             ops[name] = pool
         quant = [e for e in quant if e[0] not in ("k", "v")]
-    out = torch.empty((spec.B, spec.S, spec.Hq, spec.D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((spec.B, spec.n_q, spec.Hq, spec.D), dtype=torch.bfloat16, device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -242,7 +243,7 @@ def main():
         "vs_baseline": None,
         "dtype": f"{qk_fmt}-qk/{pv_fmt}-pv",
         "data": "synthetic",
-        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "Sq": spec.S, "Skv": spec.S,
+        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "Sq": spec.n_q, "Skv": spec.S,
                    "d": spec.D, "q": spec.q_fmt, "k": spec.k_fmt, "v": spec.v_fmt, "p": spec.v_fmt,
                    "causal": spec.causal, "block_sparse": spec.masked, "paged": spec.paged,
                    "unmasked_pairs": pairs, "flop_per_step": flops},

@@ -50,6 +50,9 @@ constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per 
 #ifndef FMHA_WAVES_PER_EU_8BIT
 #define FMHA_WAVES_PER_EU_8BIT 3
 #endif
+#ifndef FMHA_HEAD_PACK
+#define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
+#endif
 #ifndef FMHA_WAVES_PER_EU_BF16
 #define FMHA_WAVES_PER_EU_BF16 2
 #endif
@@ -130,17 +133,30 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   const int m32 = lane & 31;
 
   // ---- which (batch, head, query tile) this workgroup owns
-  const int qtile = 32 * C::NW;
+  // Either NW x 32 consecutive queries of one head, or (head packing, for
+  // grouped-query attention with short or causal query ranges) the same 32
+  // queries of NW query heads that share one KV head: every wave then needs
+  // the same keys and K/V tiles serve NW heads at once.
+  const bool pack = !C::MASKED && a.pack_heads;
+  const int qtile = pack ? 32 : 32 * C::NW;
   const int nqt = (a.Sq + qtile - 1) / qtile;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   int qt = lin % nqt;
   if (a.causal) qt = nqt - 1 - qt;  // longest causal rows first
-  const int bh = lin / nqt;
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
+  const int rest = lin / nqt;
+  int hq, b;
+  if (pack) {
+    const int gpw = a.group / C::NW;  // workgroups per KV head and query tile
+    const int bhk = rest / gpw;
+    hq = (bhk % a.Hkv) * a.group + (rest % gpw) * C::NW + wave;
+    b = bhk / a.Hkv;
+  } else {
+    hq = rest % a.Hq;
+    b = rest / a.Hq;
+  }
   const int hk = hq / a.group;
   const int q0 = qt * qtile;
-  const int q0w = q0 + 32 * wave;
+  const int q0w = pack ? q0 : q0 + 32 * wave;
   const int qi = q0w + m32;                // this lane's query row
   const int causal_off = a.Skv - a.Sq;     // key j visible iff j <= i + causal_off
 
@@ -765,9 +781,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 }
 
 template <class C>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  const int qtile = 32 * C::NW;
-  const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B;
+hipError_t launch(const FwdArgs& args, hipStream_t stream) {
+  // Head packing where K/V reuse across the heads of a group pays: a query
+  // range shorter than one workgroup tile, or a causal one (the waves then
+  // share one diagonal instead of staggering along it).
+  FwdArgs a = args;
+  a.pack_heads = FMHA_HEAD_PACK && !C::MASKED && a.group % C::NW == 0 && (a.causal || a.Sq < 32 * C::NW);
+  const int qtile = a.pack_heads ? 32 : 32 * C::NW;
+  const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B / (a.pack_heads ? C::NW : 1);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles);
   const size_t lds = (size_t)C::LDS_BYTES + 64;  // + wave -> SIMD table

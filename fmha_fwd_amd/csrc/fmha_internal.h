@@ -42,6 +42,7 @@ struct FwdArgs {
   int page_size, num_pages;
   const float* sfs_p;   // [Hq] or null
   int clamp_p;          // P / sp may reach the E4M3 overflow range
+  int pack_heads;       // set by the launcher: a workgroup takes 32 queries of NW heads sharing a KV head
 };
 
 struct FwdKey {

@@ -16,6 +16,8 @@ Configurations (d = 128 throughout):
   sparse  B=4 H=32 S=16384  bf16 Q, E4M3 K/V in 16-token pages (random page
                             table), Q64 x KV256 block mask with 16 of 64 key
                             blocks active per query block (diagonal always)
+  gqa_chunk  the gqa inputs with only the last 256 query positions (a causal
+             prefill chunk against 8192 keys)
 """
 from dataclasses import dataclass
 
@@ -40,6 +42,11 @@ class Spec:
     paged: bool = False
     page_size: int = 16
     D: int = 128
+    sq: int = 0         # query rows when fewer than the S keys: the last sq positions (0 = S)
+
+    @property
+    def n_q(self):
+        return self.sq or self.S
 
     @property
     def q_scaled(self):
@@ -54,10 +61,12 @@ class Spec:
         return self.v_fmt != "bf16"
 
     def pairs(self):
-        """Unmasked (query, key) pairs: the FLOP count is 4 * D * pairs."""
-        per_head = self.S * self.S
+        """Unmasked (query, key) pairs: the FLOP count is 4 * D * pairs.
+        Causal is bottom-right aligned: query i of n_q sees keys <= i + S - n_q."""
+        nq = self.n_q
+        per_head = nq * self.S
         if self.causal:
-            per_head = self.S * (self.S + 1) // 2
+            per_head = nq * (self.S - nq) + nq * (nq + 1) // 2
         if self.masked:
             per_head = None
         if per_head is None:
@@ -71,6 +80,8 @@ SPECS = {
     "dit": Spec("dit", 2, 1, 40, 40, 32760, "bf16", "bf16", "e4m3"),
     "gqa": Spec("gqa", 3, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True),
     "sparse": Spec("sparse", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True, paged=True),
+    # a prefill chunk: the last 256 positions of the gqa sequence against all of its keys
+    "gqa_chunk": Spec("gqa_chunk", 5, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=256),
 }
 
 
@@ -135,6 +146,8 @@ def generate(spec):
                     mask[b, h, qb, diag] = 1
                     mask[b, h, qb, pick] = 1
         out["block_mask"] = mask
+    if spec.n_q != S:
+        q = q[:, S - spec.n_q:]
     out["q"] = to_bf16_values(q)
     out["k"] = to_bf16_values(k)
     out["v"] = to_bf16_values(v)
@@ -146,4 +159,4 @@ def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
     s = SPECS[base]
     return Spec(s.name + f"_S{S}", s.index, B or s.B, Hq or s.Hq, Hkv or s.Hkv, S, s.q_fmt, s.k_fmt, s.v_fmt,
                 kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged),
-                kw.get("page_size", s.page_size))
+                kw.get("page_size", s.page_size), sq=kw.get("sq", 0))

@@ -124,6 +124,19 @@ def test_no_valid_key_rows_are_zero():
     assert np.all(gpu[0, 128:192] == 0) and np.all(np.abs(gpu[0, :128]).sum(-1) > 0)
 
 
+@pytest.mark.parametrize("sq,S", [(1, 300), (32, 300), (40, 511), (96, 700)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_query_chunk_gqa(sq, S, causal):
+    # fewer queries than keys (a prefill chunk, bottom-right causal); with four
+    # query heads per KV head the kernel packs heads into one workgroup
+    _run_small(W.small_spec("gqa", S, B=1, Hq=8, Hkv=2, causal=causal, sq=sq))
+
+
+@pytest.mark.parametrize("S", [1, 130, 320])
+def test_small_causal_gqa_packed(S):
+    _run_small(W.small_spec("gqa", S, B=2, Hq=8, Hkv=2, causal=True))
+
+
 def test_deterministic():
     spec = W.small_spec("gqa", 700, B=1, Hq=8, Hkv=2, causal=True)
     data = W.generate(spec)
@@ -140,6 +153,7 @@ FULL = [
     ("dit", [(0, 0), (0, 39)], "sample"),
     ("gqa", [(0, 0), (0, 7), (1, 63)], "sample"),
     ("sparse", [(0, 0), (3, 31)], "sample"),
+    ("gqa_chunk", [(0, 0), (1, 63)], None),
 ]
 
 
@@ -156,7 +170,7 @@ def test_full_workload_sampled_rows(name, heads, rows, workload_cache):
     print(f"fwd full {name}", flush=True)
     data = workload_cache(name)
     gpu, _ = Hn.gpu_run(spec, data)
-    r = None if rows is None else _sample_rows(spec.S)
+    r = None if rows is None else _sample_rows(spec.n_q)
     hq_list = None if heads is None else sorted({h for _, h in heads})
     hk_list = None if heads is None else sorted({h // (spec.Hq // spec.Hkv) for h in hq_list})
     ops = Hn.oracle_operands(spec, data, heads_q=hq_list, heads_kv=hk_list)
