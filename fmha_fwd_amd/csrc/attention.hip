@@ -193,9 +193,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // LDS pointers stay in the LDS address space (no generic-pointer casts).
   lds_u8* const kbuf0 = (lds_u8*)smem;
   lds_u8* const vbuf0 = kbuf0 + 2 * C::K_BUF;
-  // Every wave issues the same number of wave-wide DMA operations per
-  // sub-tile (slots past the tile repeat its last operation: identical bytes
-  // to the same place), so the loop body has no per-wave branches.  Per-lane
+  // Copy j of a sub-tile (1 KB, one wave-wide DMA operation) is issued by
+  // wave j % NW as its slot j / NW; contiguous K/V skip the slots past the
+  // last copy (a wave-uniform branch), paged K/V repeat the last copy there
+  // (identical bytes to the same place).  Per-lane
   // source offsets within a tile are fixed; contiguous K/V go through a
   // buffer resource whose range ends at the last token, so rows past the end
   // of the sequence read as zeros.  K rows are stored in MFMA row order: LDS
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
 #pragma unroll
       for (int sl = 0; sl < KSL; ++sl) {
-        const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
+        const int j = wave + sl * C::NW;
+        if (C::K_DMA_OPS % C::NW == 0 || sl + 1 < KSL || j < C::K_DMA_OPS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
 #pragma unroll
@@ -313,8 +315,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       const auto rs = tile_rsrc(vbase, a.v_ss, kv0);
 #pragma unroll
       for (int sl = 0; sl < VSL; ++sl) {
-        const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], 0, 0, 0);
+        const int j = wave + sl * C::NW;
+        if (C::V_DMA_OPS % C::NW == 0 || sl + 1 < VSL || j < C::V_DMA_OPS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], 0, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
 #pragma unroll
