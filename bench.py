@@ -107,6 +107,23 @@ def cpu_baseline(spec, data, budget_s=12.0):
 COPY_BYTES = 1 << 30
 
 
+def copy_bandwidth(torch, reps=5):
+    """GB/s (read + write bytes) of a plain 1 GiB device-to-device copy: the
+    practical HBM ceiling next to the 8 TB/s published peak."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * COPY_BYTES * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def calibrate_copy(torch, steps):
     """A plain copy of COPY_BYTES (read once, written once) for the byte
     counters: FETCH_SIZE / WRITE_SIZE of this kernel against COPY_BYTES give
@@ -214,6 +231,7 @@ def main():
     fwd_ms = float(np.mean(f_ms))
     fwd_median, fwd_min = float(np.median(f_ms)), float(np.min(f_ms))
 
+    copy_gbs = copy_bandwidth(torch)
     pairs = pair_count(spec, data)
     flops = 4.0 * spec.D * pairs
     qk_fmt = "bf16" if spec.q_fmt == "bf16" or spec.k_fmt == "bf16" else spec.q_fmt
@@ -260,6 +278,8 @@ def main():
         "fwd_tflops_at_min": flops / (fwd_min * 1e-3) / 1e12,
         "quantize_ms": float(np.mean(q_ms)) if quant else 0.0,
         "quantize_gbs": (quant_bytes / (np.mean(q_ms) * 1e-3) / 1e9) if quant else None,
+        "quantize_frac_of_hbm_peak": (quant_bytes / (np.mean(q_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS) if quant else None,
+        "hbm_copy_gbs": copy_gbs,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(spec, data)
