@@ -14,9 +14,10 @@
 //    최적화", 코드 분석 1-2: Q64 x KV256 block-sparse masks, paged K/V.
 //
 // Design for CDNA4 (not a translation of the pages' Hopper/Blackwell kernels):
-//  * One workgroup = NW wavefronts x 32 queries of one (batch, head).  K and V
-//    stream through LDS in 64-key sub-tiles, double-buffered; the Q tile stays
-//    in VGPRs for the whole key loop.
+//  * One workgroup = NW wavefronts x 32 queries of one (batch, head), or the
+//    same 32 queries of NW query heads that share a KV head (grouped-query
+//    head packing).  K and V stream through LDS in 64-key sub-tiles,
+//    double-buffered; the Q tile stays in VGPRs for the whole key loop.
 //  * The score tile is computed transposed, S^T = K Q^T, on 32x32 MFMA tiles,
 //    so every lane owns one query row: the row max / sum are in-register
 //    reductions plus one exchange with lane l ^ 32, and the per-row lazy
@@ -25,10 +26,15 @@
 //    S^T accumulator of lane group g holds 16 consecutive keys; those P values
 //    are packed in place into the B operand of O^T += V^T P^T, and V^T is read
 //    from LDS with the gfx950 transposing loads (ds_read_b64_tr_b8 / _b16).
-//  * The lazy decision is per row and per 64-key sub-tile; the branch is taken
-//    by the whole wave when any row triggers, with factor 1 for the others.
-//  * V's per-64-token scale multiplies each sub-tile's PV partial product
-//    before it is added to O (scales applied after BMM2).
+//  * The lazy decision is per row and per 64-key sub-tile, branch-free: rows
+//    that do not trigger take factor 1.
+//  * V's per-64-token scale is applied after BMM2: O is kept in units of the
+//    current sub-tile's V scale, so one multiply per O element folds the
+//    lazy factor and the change of scale, and the PV MFMA accumulates codes
+//    x codes into O (or, when the scales span more than 2^64, each partial
+//    product is scaled into O).
+//  * Row sums of an E4M3 P come from one more MFMA (a 0/1 matrix times the P
+//    operand) instead of VALU conversions and additions.
 //  * sfs_p cancels between numerator and denominator, so it enters only the
 //    quantisation of P (exp2 argument shifted by log2 sfs_p).
 #include <type_traits>
@@ -50,11 +56,11 @@ constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per 
 #ifndef FMHA_WAVES_PER_EU_8BIT
 #define FMHA_WAVES_PER_EU_8BIT 3
 #endif
-#ifndef FMHA_HEAD_PACK
-#define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
-#endif
 #ifndef FMHA_WAVES_PER_EU_BF16
 #define FMHA_WAVES_PER_EU_BF16 2
+#endif
+#ifndef FMHA_HEAD_PACK
+#define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
 #endif
 constexpr float kInf = __builtin_huge_valf();
 
@@ -524,8 +530,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     float f;           // product scale (slow path only)
   };
 
-  // Softmax of one sub-tile in eight stages, so that the pipelined loop can
-  // place each next to a group of MFMAs:
+  // Softmax of one sub-tile, written as eight stages of separable work:
   //   0: row max, lazy decision, rescale of den (and of O off the fast path);
   //   1-2: rescale of O, two d-tiles each (fast V-reference path);
   //   3-6: P = 2^(s2 - m) / sp for eight keys each, clamped to the E4M3 range
