@@ -97,7 +97,11 @@ def cpu_baseline(spec, data, budget_s=12.0):
         else:
             pairs_done += len(rows) * spec.S
     flops = 4.0 * spec.D * pairs_done
+    rows_total = spec.B * spec.Hq * nq
     return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "rows_per_s": rows_done / t_att,
+            "extrapolated_full_s": 4.0 * spec.D * (pair_count(spec, data) or 0) / (flops / t_att),
+            "rows_total": rows_total,
             "sample": f"{rows_done} random query rows of head 0 (batch 0), all {spec.S} keys each, lazy E4M3-P "
                       f"oracle in fp64 numpy; operand dequantisation ({t_prep:.1f} s) not counted; "
                       f"{t_att:.1f} s of CPU time",
@@ -141,7 +145,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
