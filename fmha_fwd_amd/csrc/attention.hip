@@ -180,9 +180,33 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 
   const uint8_t* mask_row = nullptr;
   if (C::MASKED) mask_row = a.mask + (int64_t)b * a.m_sb + (int64_t)hq * a.m_sh + (int64_t)(q0 / 64) * a.m_sqb;
+  // Block mask: the active key blocks of this workgroup's query block, 64
+  // blocks at a time, as a wave-uniform bit mask (one mask byte per lane,
+  // then a ballot), so skipping inactive blocks costs no memory round trip.
+  const int kvsub = C::MASKED ? a.mask_kv_sub : 1;  // sub-tiles per mask key block
+  const int n_mkb = C::MASKED ? (a.Skv + kSub * kvsub - 1) / (kSub * kvsub) : 0;
+  uint64_t mbits = 0;
+  int mb_base = -64;  // mbits bit i: mask key block mb_base + i is active
+  // First sub-tile at or after t whose mask block is active (n_sub if none).
   auto next_sub = [&](int t) {
-    if (C::MASKED) {
-      while (t < n_sub && mask_row[t / a.mask_kv_sub] == 0) ++t;
+    if constexpr (C::MASKED) {
+      if (t >= n_sub) return n_sub;
+      int mb = t / kvsub;
+      while (mb * kvsub < n_sub) {
+        if (mb - mb_base >= 64) {
+          mb_base = mb;
+          const int i = mb + lane;
+          mbits = __ballot(i < n_mkb && mask_row[i] != 0);
+        }
+        const uint64_t ahead = mbits >> (mb - mb_base);
+        if (ahead != 0) {
+          mb += __builtin_ctzll(ahead);
+          const int r = max(t, mb * kvsub);
+          return r < n_sub ? r : n_sub;
+        }
+        mb = mb_base + 64;
+      }
+      return n_sub;
     }
     return t;
   };

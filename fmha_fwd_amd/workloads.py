@@ -154,6 +154,18 @@ def generate(spec):
     return out
 
 
+def random_block_mask(B, Hq, Sq, Skv, block_kv, density, stream, empty_q_blocks=()):
+    """uint8 [B, Hq, ceil(Sq/64), ceil(Skv/block_kv)] block mask with each
+    block active with probability `density` (seeded by `stream`); the query
+    blocks listed in `empty_q_blocks` see no key at all."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=(1000 + stream,))))
+    nqb, nkb = -(-Sq // 64), -(-Skv // block_kv)
+    mask = (rng.random((B, Hq, nqb, nkb)) < density).astype(np.uint8)
+    for qb in empty_q_blocks:
+        mask[:, :, qb] = 0
+    return mask
+
+
 def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
     """A reduced-size variant of a configuration (same formats and options)."""
     s = SPECS[base]

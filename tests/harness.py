@@ -51,10 +51,10 @@ def oracle_output(spec, data, operands, rows=None, heads=None, quantized=True, *
                      p_format=p_fmt, rows=rows, heads=heads, flip_eps=FLIP_EPS, **kw)
 
 
-def unquantized_output(spec, data, rows=None, heads=None):
+def unquantized_output(spec, data, rows=None, heads=None, **kw):
     qd, kd, vd = (data[n].astype(np.float64) for n in ("q", "k", "v"))
     return attention(qd, kd, vd, causal=spec.causal, block_mask=data.get("block_mask"), mode="exact",
-                     p_format=None, rows=rows, heads=heads)
+                     p_format=None, rows=rows, heads=heads, **kw)
 
 
 # ------------------------------------------------------------------ GPU side

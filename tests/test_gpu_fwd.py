@@ -124,6 +124,29 @@ def test_no_valid_key_rows_are_zero():
     assert np.all(gpu[0, 128:192] == 0) and np.all(np.abs(gpu[0, :128]).sum(-1) > 0)
 
 
+@pytest.mark.parametrize("block_kv,S,paged,causal", [(64, 4500, False, False), (192, 1000, True, False),
+                                                     (512, 1500, False, True), (64, 4200, True, True)])
+def test_mask_key_block_sizes(block_kv, S, paged, causal):
+    # key blocks of 1, 3 and 8 sub-tiles; more than 64 key blocks per query
+    # block; query blocks 1 and the last with no active key block
+    spec = W.small_spec("sparse", S, B=1, Hq=2, Hkv=1, paged=paged, causal=causal)
+    print(f"fwd mask blocks {spec} block_kv={block_kv}", flush=True)
+    data = W.generate(spec)
+    nqb = -(-S // 64)
+    data["block_mask"] = W.random_block_mask(1, 2, S, S, block_kv, 0.3, stream=block_kv + S,
+                                             empty_q_blocks=(1, nqb - 1))
+    gpu, _ = Hn.gpu_run(spec, data, mask_block=(64, block_kv))
+    rows = _sample_rows(S)
+    rows = np.union1d(rows, np.arange(64, 128))
+    ops = Hn.oracle_operands(spec, data)
+    ref = Hn.oracle_output(spec, data, ops, rows=rows, mask_block_kv=block_kv)
+    unq = Hn.unquantized_output(spec, data, rows=rows, mask_block_kv=block_kv)
+    g = gpu[:, rows]
+    assert np.all(g[:, np.isin(rows, np.arange(64, 128))] == 0)
+    assert np.all(g[:, rows >= (nqb - 1) * 64] == 0)
+    Hn.assert_parity(g, ref, unq, what=f"mask blocks {block_kv}")
+
+
 @pytest.mark.parametrize("sq,S", [(1, 300), (32, 300), (40, 511), (96, 700)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_query_chunk_gqa(sq, S, causal):
