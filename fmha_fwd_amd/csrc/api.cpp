@@ -202,6 +202,11 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   a.num_pages = paged ? p->num_pages : 0;
   // P <= 2^tau / sfs_p; E4M3 conversion needs a clamp once that can reach 464.
   a.clamp_p = (p->sfs_p != nullptr) || (p->lazy_rescale_log2 > 8.5f);
+  // Contiguous K/V: with positive token strides and a sequence (plus one
+  // sub-tile of overrun) under 2^31 bytes, every tile offset fits the
+  // buffer's 32-bit offset, so one resource per workgroup serves all tiles.
+  a.kv_whole_rsrc = !paged && a.k_ss > 0 && a.v_ss > 0 &&
+                    (int64_t)(p->Skv + 64) * std::max(a.k_ss, a.v_ss) < ((int64_t)1 << 31);
   return hip_status(fmha::launch_fwd(key, a, static_cast<hipStream_t>(stream)), "fwd launch");
 }
 

@@ -294,46 +294,66 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * ss), 0, nrec, 0x00020000);
   };
-  // Source of one paged copy (slot bit field `idx`, in-page offset `off`).
-  // In the last sub-tile a row past the end takes the last token's page slot
-  // and offset (row `rl` of the sub-tile).
-  auto paged_src = [&](const uint8_t* base, int64_t sb, int64_t ss, int kv0, int pages, int idx, uint32_t off,
-                       bool past_end, int rl, int ch) {
+  // When the whole sequence of this (batch, KV head) spans under 2^31 bytes,
+  // one resource covers it and a tile's start goes into the scalar offset
+  // (which the range check counts like the rest of the offset); otherwise
+  // every tile gets a resource of its own.
+  const bool kv_whole = !C::PAGED && a.kv_whole_rsrc;
+  const auto k_rs_all = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, kv_whole ? a.Skv * (int)a.k_ss : 0, 0x00020000);
+  const auto v_rs_all = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kv_whole ? a.Skv * (int)a.v_ss : 0, 0x00020000);
+  // Paged: address of the first row of sub-tile t (first key kv0) in page
+  // slot lane & 3, whose page number this lane holds; one 64-bit product per
+  // sub-tile and tensor, shared by every copy through ds_bpermute.
+  auto page_addr = [&](const uint8_t* base, int64_t sb, int64_t ss, int kv0, int page) {
+    const int64_t in_page = (int64_t)(kv0 & (a.page_size - 1)) * ss;  // pages longer than a sub-tile
+    return (uint64_t)(base + in_page) + (uint64_t)(uint32_t)page * (uint64_t)sb;
+  };
+  // Source of one paged copy (slot bit field `idx`, in-page offset `off`)
+  // from the page addresses `pa`.  In the last sub-tile a row past the end
+  // takes the last token's page slot and offset (row `rl` of the sub-tile).
+  auto paged_src = [&](uint64_t pa, int64_t ss, int idx, uint32_t off, bool past_end, int rl, int ch) {
     int ps = (int)(pslot_bits >> (2 * idx)) & 3;
     if (past_end) {
       ps = rl >> tshift;
       off = (uint32_t)((rl & tmask) * ss) + ch * 16;
     }
-    const int page = __builtin_amdgcn_ds_bpermute(ps << 2, pages);
-    const int64_t in_page = (int64_t)(kv0 & (a.page_size - 1)) * ss;  // pages longer than a sub-tile
-    return base + (int64_t)page * sb + in_page + off;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(ps << 2, (int)(uint32_t)pa);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(ps << 2, (int)(uint32_t)(pa >> 32));
+    return (const uint8_t*)((((uint64_t)hi << 32) | lo) + off);
   };
   auto dma_k = [&](int t, int buf, int pages) {
     const int kv0 = t * kSub;
     lds_u8* dst = kbuf0 + buf * C::K_BUF;
     if constexpr (!C::PAGED) {
-      const auto rs = tile_rsrc(kbase, a.k_ss, kv0);
+      const auto rs = kv_whole ? k_rs_all : tile_rsrc(kbase, a.k_ss, kv0);
+      const int soff = kv_whole ? kv0 * (int)a.k_ss : 0;
 #pragma unroll
       for (int sl = 0; sl < KSL; ++sl) {
         const int j = wave + sl * C::NW;
         if (C::K_DMA_OPS % C::NW == 0 || sl + 1 < KSL || j < C::K_DMA_OPS)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], soff, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
+      // all page exchanges first, so their latencies overlap
+      const uint64_t pa = page_addr(kbase, a.k_sb, a.k_ss, kv0, pages);
+      const uint8_t* src[KSL];
+#pragma unroll
+      for (int sl = 0; sl < KSL; ++sl) src[sl] = paged_src(pa, a.k_ss, sl, k_src[sl], false, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int sl = 0; sl < KSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
-        const uint8_t* src = paged_src(kbase, a.k_sb, a.k_ss, kv0, pages, sl, k_src[sl], false, 0, 0);
-        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src[sl], FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     } else {
       const int rl = a.Skv - 1 - kv0;
+      const uint64_t pa = page_addr(kbase, a.k_sb, a.k_ss, kv0, pages);
 #pragma unroll
       for (int sl = 0; sl < KSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
         int ch;
         const int row = k_copy_row(j, ch);
-        const uint8_t* src = paged_src(kbase, a.k_sb, a.k_ss, kv0, pages, sl, k_src[sl], row > rl, rl, ch);
+        const uint8_t* src = paged_src(pa, a.k_ss, sl, k_src[sl], row > rl, rl, ch);
         __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }
@@ -342,28 +362,34 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     const int kv0 = t * kSub;
     lds_u8* dst = vbuf0 + buf * C::V_BUF;
     if constexpr (!C::PAGED) {
-      const auto rs = tile_rsrc(vbase, a.v_ss, kv0);
+      const auto rs = kv_whole ? v_rs_all : tile_rsrc(vbase, a.v_ss, kv0);
+      const int soff = kv_whole ? kv0 * (int)a.v_ss : 0;
 #pragma unroll
       for (int sl = 0; sl < VSL; ++sl) {
         const int j = wave + sl * C::NW;
         if (C::V_DMA_OPS % C::NW == 0 || sl + 1 < VSL || j < C::V_DMA_OPS)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], soff, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
+      const uint64_t pa = page_addr(vbase, a.v_sb, a.v_ss, kv0, pages);
+      const uint8_t* src[VSL];
+#pragma unroll
+      for (int sl = 0; sl < VSL; ++sl) src[sl] = paged_src(pa, a.v_ss, KSL + sl, v_src[sl], false, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int sl = 0; sl < VSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
-        const uint8_t* src = paged_src(vbase, a.v_sb, a.v_ss, kv0, pages, KSL + sl, v_src[sl], false, 0, 0);
-        __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src[sl], FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     } else {
       const int rl = a.Skv - 1 - kv0;
+      const uint64_t pa = page_addr(vbase, a.v_sb, a.v_ss, kv0, pages);
 #pragma unroll
       for (int sl = 0; sl < VSL; ++sl) {
         const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
         int ch;
         const int row = v_copy_row(j, ch);
-        const uint8_t* src = paged_src(vbase, a.v_sb, a.v_ss, kv0, pages, KSL + sl, v_src[sl], row > rl, rl, ch);
+        const uint8_t* src = paged_src(pa, a.v_ss, KSL + sl, v_src[sl], row > rl, rl, ch);
         __builtin_amdgcn_global_load_lds(src, FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     }

@@ -43,6 +43,7 @@ struct FwdArgs {
   const float* sfs_p;   // [Hq] or null
   int clamp_p;          // P / sp may reach the E4M3 overflow range
   int pack_heads;       // set by the launcher: a workgroup takes 32 queries of NW heads sharing a KV head
+  int kv_whole_rsrc;    // contiguous K/V of one (batch, head) span < 2^31 bytes: one buffer resource each
 };
 
 struct FwdKey {

@@ -115,6 +115,30 @@ def test_strided_q_and_output():
     assert torch.count_nonzero(out[:, :, 0]) == 0 and torch.count_nonzero(out[:, :, 3]) == 0
 
 
+def test_kv_sequence_beyond_2gib():
+    # K/V token strides of 4 MiB: each sequence spans more than 2^31 bytes,
+    # so every tile gets a buffer resource of its own
+    import fmha_fwd_amd as F
+    spec = W.small_spec("dit", 640, B=1, Hq=2, Hkv=2)
+    print(f"fwd {spec} with 4 MiB K/V token strides", flush=True)
+    data = W.generate(spec)
+    q = Hn.to_gpu_bf16(data["q"])
+    v_codes, sv = F.quantize_blocks(Hn.to_gpu_bf16(data["v"]), "e4m3")
+    stride = 1 << 22
+    kbig = torch.empty(640 * stride // 2, dtype=torch.bfloat16, device="cuda")
+    k = kbig.as_strided((1, 640, 2, 128), (640 * stride // 2, stride // 2, 128, 1))
+    k.copy_(Hn.to_gpu_bf16(data["k"]))
+    vbig = torch.empty(640 * stride, dtype=torch.uint8, device="cuda")
+    v = vbig.as_strided((1, 640, 2, 128), (640 * stride, stride, 128, 1))
+    v.copy_(v_codes.view(torch.uint8))
+    o = F.fwd(q, k, v.view(torch.float8_e4m3fn), sfs_v=sv)
+    torch.cuda.synchronize()
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(o.float().cpu().numpy(), Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data),
+                     what="2 GiB K/V span")
+    del kbig, vbig
+
+
 def test_no_valid_key_rows_are_zero():
     import fmha_fwd_amd as F
     spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)
