@@ -849,7 +849,7 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B / (a.pack_heads ? C::NW : 1);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles);
-  const size_t lds = (size_t)C::LDS_BYTES + 64;  // + wave -> SIMD table
+  const size_t lds = (size_t)C::LDS_BYTES;
   static bool configured = false;  // benign race: the attribute is idempotent
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
