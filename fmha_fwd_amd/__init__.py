@@ -44,6 +44,7 @@ class FmhaFwdParams(ctypes.Structure):
         ("page_table_stride_b", ctypes.c_int64),
         ("page_size", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
+        ("sfs_o", ctypes.c_void_p),
     ]
 
 
@@ -138,8 +139,10 @@ def quantize_blocks(x, dtype="e4m3", *, codes=None, scales=None, stream=None):
 
 def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False, block_mask=None,
         mask_block=(64, 256), page_table=None, page_size=16, seq_len_kv=None, softmax_scale=None,
-        lazy_rescale_log2=8.0, out=None, stream=None):
-    """Attention forward; returns o (bf16 [B, Sq, Hq, 128]).
+        lazy_rescale_log2=8.0, out=None, out_dtype="bf16", sfs_o=None, stream=None):
+    """Attention forward; returns o ([B, Sq, Hq, 128], bf16, or E4M3 when
+    out_dtype is "e4m3" or `out` is float8_e4m3fn; sfs_o: fp32 [Hq] output
+    scale of an E4M3 o, o = encode(O / sfs_o)).
 
     q: [B, Sq, Hq, 128] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, 128],
     or with page_table (int32 [B, pages]) pools [num_pages, page_size, Hkv, 128]
@@ -148,7 +151,7 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
     last dim contiguous).
     """
     import torch
-    _require_cuda(q, k, v, sfs_q, sfs_k, sfs_v, sfs_p, block_mask, page_table, out)
+    _require_cuda(q, k, v, sfs_q, sfs_k, sfs_v, sfs_p, block_mask, page_table, out, sfs_o)
     B, Sq, Hq, D = q.shape
     if page_table is None:
         Skv, Hkv = k.shape[1], k.shape[2]
@@ -157,8 +160,9 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
             raise ValueError("seq_len_kv is required with a page table")
         Skv, Hkv = int(seq_len_kv), k.shape[2]
     if out is None:
-        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
-    for s in (sfs_q, sfs_k, sfs_v, sfs_p):
+        odt = {"bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[out_dtype]
+        out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
+    for s in (sfs_q, sfs_k, sfs_v, sfs_p, sfs_o):
         if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()):
             raise ValueError("scale factors must be contiguous float32")
     p = FmhaFwdParams()
@@ -170,6 +174,7 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
     p.sage_block_k = 64 if sfs_k is not None else 0
     p.sage_block_v = 64 if sfs_v is not None else 0
     p.sfs_p = _ptr(sfs_p)
+    p.sfs_o = _ptr(sfs_o)
     p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
     p.lazy_rescale_log2 = float(lazy_rescale_log2)
     p.causal = 1 if causal else 0

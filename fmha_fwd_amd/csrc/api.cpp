@@ -6,7 +6,9 @@
 // the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -66,7 +68,7 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-uint32_t fmha_abi_version(void) { return 0x000100u; }
+uint32_t fmha_abi_version(void) { return 0x000200u; }
 
 const char* fmha_last_error(void) { return g_last_error.c_str(); }
 
@@ -107,14 +109,20 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes, float* 
 
 int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   if (!p) return fail(FMHA_ERR_INVALID, "fwd: null params");
-  if (p->struct_size != sizeof(fmha_fwd_params))
-    return fail(FMHA_ERR_INVALID, "fwd: struct_size %u does not match this library (%zu)", p->struct_size,
-                sizeof(fmha_fwd_params));
+  // this layout, or the previous one (which ends before sfs_o)
+  const size_t prev_size = offsetof(fmha_fwd_params, sfs_o);
+  if (p->struct_size != sizeof(fmha_fwd_params) && p->struct_size != prev_size)
+    return fail(FMHA_ERR_INVALID, "fwd: struct_size %u does not match this library (%zu or %zu)", p->struct_size,
+                sizeof(fmha_fwd_params), prev_size);
+  const float* sfs_o = p->struct_size == sizeof(fmha_fwd_params) ? p->sfs_o : nullptr;
   if (p->B < 0 || p->Sq < 0 || p->Skv < 0) return fail(FMHA_ERR_INVALID, "fwd: negative size");
   if (p->Hq < 1 || p->Hkv < 1) return fail(FMHA_ERR_INVALID, "fwd: Hq and Hkv must be >= 1");
   if (p->Hq % p->Hkv != 0) return fail(FMHA_ERR_INVALID, "fwd: Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
   if (p->D != 128) return fail(FMHA_ERR_UNSUPPORTED, "fwd: D=%d (only 128 is supported)", p->D);
-  if (p->o.dtype != FMHA_DT_BF16) return fail(FMHA_ERR_UNSUPPORTED, "fwd: o must be bf16");
+  if (p->o.dtype != FMHA_DT_BF16 && p->o.dtype != FMHA_DT_E4M3)
+    return fail(FMHA_ERR_UNSUPPORTED, "fwd: o must be bf16 or e4m3");
+  if (sfs_o && p->o.dtype != FMHA_DT_E4M3) return fail(FMHA_ERR_INVALID, "fwd: sfs_o given for a bf16 o");
+  if (sfs_o && reinterpret_cast<uintptr_t>(sfs_o) % 4) return fail(FMHA_ERR_INVALID, "fwd: sfs_o misaligned");
   if (p->v.dtype == FMHA_DT_INT8) return fail(FMHA_ERR_UNSUPPORTED, "fwd: int8 V is not supported");
   const bool empty = (int64_t)p->B * p->Sq == 0;
   const bool paged = p->page_table != nullptr;
@@ -184,7 +192,10 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   a.v = static_cast<const uint8_t*>(p->v.ptr);
   a.v_sb = p->v.stride_b * ve; a.v_ss = p->v.stride_s * ve; a.v_sh = p->v.stride_h * ve;
   a.o = static_cast<uint8_t*>(p->o.ptr);
-  a.o_sb = p->o.stride_b * 2; a.o_ss = p->o.stride_s * 2; a.o_sh = p->o.stride_h * 2;
+  const int oe = elem_size(p->o.dtype);
+  a.o_sb = p->o.stride_b * oe; a.o_ss = p->o.stride_s * oe; a.o_sh = p->o.stride_h * oe;
+  a.o_fp8 = p->o.dtype == FMHA_DT_E4M3;
+  a.sfs_o = sfs_o;
   a.sfs_q = p->sfs_q; a.sfs_k = p->sfs_k; a.sfs_v = p->sfs_v; a.sfs_p = p->sfs_p;
   a.B = p->B; a.Sq = p->Sq; a.Skv = p->Skv; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
   a.nblk_q = (p->Sq + 63) / 64;

@@ -816,13 +816,30 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     else run(std::false_type{}, std::true_type{});
   }
 
-  // ---- epilogue: O = num / den in bf16; rows without a valid key give 0
+  // ---- epilogue: O = num / den in bf16 (or E4M3); rows without a valid key give 0
   float dt;
   if constexpr (C::VF == FMT_E4M3) dt = den_acc[0];
   else dt = den + __shfl_xor(den, 32, 64);
   const float inv = dt > 0.0f ? sv_ref / dt : 0.0f;
   if (qi >= a.Sq) return;
   uint8_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)qi * a.o_ss;
+  if (a.o_fp8) {
+    // E4M3 output: encode(O / sfs_o), nearest-even, saturating at +-448
+    const float f = a.sfs_o ? inv / a.sfs_o[hq] : inv;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(o[d][4 * a4 + i] * f, -448.0f), 448.0f);
+        int pk = pack_e4m3<false>(x[0], x[1], 0);
+        pk = pack_e4m3<true>(x[2], x[3], pk);
+        *(int*)(op + 32 * d + 8 * a4 + 4 * g) = pk;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll

@@ -44,6 +44,8 @@ struct FwdArgs {
   int clamp_p;          // P / sp may reach the E4M3 overflow range
   int pack_heads;       // set by the launcher: a workgroup takes 32 queries of NW heads sharing a KV head
   int kv_whole_rsrc;    // contiguous K/V of one (batch, head) span < 2^31 bytes: one buffer resource each
+  int o_fp8;            // o is E4M3: encode(O / sfs_o[h])
+  const float* sfs_o;   // [Hq] or null (= 1)
 };
 
 struct FwdKey {

@@ -109,7 +109,7 @@ typedef struct {
   uint32_t struct_size;
   int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128; Hq % Hkv == 0; query head h
                                       reads key/value head h / (Hq / Hkv) */
-  /* q: [B, Sq, Hq, D]; o: [B, Sq, Hq, D] bf16 (written).
+  /* q: [B, Sq, Hq, D]; o: [B, Sq, Hq, D] bf16 or E4M3 (written).
    * k, v contiguous-cache case: [B, Skv, Hkv, D].
    * k, v paged case (page_table != NULL): pools [num_pages, page_size, Hkv, D]
    * where stride_b is the stride between pages and stride_s the stride
@@ -148,6 +148,11 @@ typedef struct {
   int64_t page_table_stride_b;
   int32_t page_size;         /* tokens per page: a power of two >= 16 (16 in the block-sparse workload) */
   int32_t num_pages;
+  /* Static per-query-head output scale, fp32 [Hq], for an E4M3 o, or NULL
+   * (= 1.0): o = encode(O / sfs_o[h]), E4M3 nearest-even, saturating at
+   * +-448.  Must be NULL for a bf16 o.  A caller built against the previous
+   * layout (struct_size = offsetof(fmha_fwd_params, sfs_o)) gets NULL. */
+  const float* sfs_o;
 } fmha_fwd_params;
 
 /*
@@ -161,7 +166,8 @@ typedef struct {
  * running numerator and denominator multiplied by 2^(m - t).
  *   P = 2^(s2 - m);  w = Qp(P / sp) * sp  (Qp = E4M3 for an E4M3 V, bf16
  *   for a bf16 V; sp = sfs_p[h] or 1);  num += w V[j] * sfs_v;  den += w.
- *   o[i] = bf16(num / den), or 0 for a row without a valid key.
+ *   o[i] = bf16(num / den), or 0 for a row without a valid key; an E4M3 o
+ *   holds encode(num / den / so) instead (so = sfs_o[h] or 1).
  *
  * Supported (q, k, v) formats, with the scaled operands in brackets:
  *   (bf16, bf16, bf16)          unscaled
@@ -169,7 +175,8 @@ typedef struct {
  *   (bf16, bf16, e4m3)          [v] or none
  *   (e4m3, e4m3, e4m3)          [q, k, v]
  *   (bf16, e4m3, e4m3)          [k, v]
- * o is always bf16.  Other combinations return FMHA_ERR_UNSUPPORTED.
+ * o is bf16 or E4M3 for each of them.  Other combinations return
+ * FMHA_ERR_UNSUPPORTED.
  */
 int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream);
 

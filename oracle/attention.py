@@ -24,6 +24,10 @@ What is computed (the readings are stated where the pages leave a step open):
 6. num += sum_j w_j V_j and den += sum_j w_j (the denominator uses the same
    quantised weights as the numerator).
 7. O = num / den; a row with no valid key gives 0.
+8. Optional E4M3 output (``output_e4m3``): the #5900 page's reviewer-feedback
+   paragraph names an FP8 output of the kernel without saying how it is
+   scaled; read here as a static per-head output scale, like sfs_p:
+   o = encode(O / so), nearest-even, saturating at +-448.
 
 ``mode="exact"`` replaces step 4 by the true row maximum (no rescaling);
 ``p_format=None`` skips step 5.  Together they give plain softmax attention.
@@ -42,7 +46,7 @@ import math
 
 import numpy as np
 
-from .codecs import bf16_round64, e4m3_decode, e4m3_round, rounding_gap
+from .codecs import bf16_round64, e4m3_decode, e4m3_encode, e4m3_round, rounding_gap
 
 LOG2E = 1.0 / math.log(2.0)
 
@@ -221,3 +225,11 @@ def attention(qd, kd, vd, *, softmax_scale=None, causal=False, block_mask=None,
         else:
             out[b, :, hq], bound[b, :, hq] = r
     return out if flip_eps is None else (out, bound)
+
+
+def output_e4m3(o, sfs_o=None):
+    """Step 8: E4M3 codes (uint8) of an output O [B, S, Hq, D],
+    encode(O / so[h]) with so = sfs_o[h] (fp32 [Hq]) or 1."""
+    o = np.asarray(o, dtype=np.float64)
+    so = np.ones(o.shape[2]) if sfs_o is None else np.asarray(sfs_o, dtype=np.float64)
+    return e4m3_encode(o / so[None, None, :, None])

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in syms, name
         assert getattr(lib, name) is not None
-    assert lib.fmha_abi_version() == 0x000100
+    assert lib.fmha_abi_version() == 0x000200
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -95,7 +95,9 @@ def _call(lib, p):
     (dict(q=_tensor(F.FMHA_DT_BF16, ptr=FAKE + 8)), F.FMHA_ERR_INVALID, "aligned"),
     (dict(q=_tensor(F.FMHA_DT_BF16, ptr=0)), F.FMHA_ERR_INVALID, "null"),
     (dict(k=_tensor(F.FMHA_DT_BF16, ss=100)), F.FMHA_ERR_INVALID, "stride_s"),
-    (dict(o=_tensor(F.FMHA_DT_E4M3)), F.FMHA_ERR_UNSUPPORTED, "bf16"),
+    (dict(o=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "bf16 or e4m3"),
+    (dict(sfs_o=FAKE), F.FMHA_ERR_INVALID, "sfs_o given"),
+    (dict(o=_tensor(F.FMHA_DT_E4M3), sfs_o=FAKE + 2), F.FMHA_ERR_INVALID, "sfs_o misaligned"),
     (dict(v=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "int8 V"),
     (dict(q=_tensor(7)), F.FMHA_ERR_INVALID, "dtype"),
     (dict(sage_block_v=32), F.FMHA_ERR_UNSUPPORTED, "sage_block_v"),
@@ -116,6 +118,16 @@ def _call(lib, p):
 def test_fwd_rejects_bad_arguments_before_any_hip_call(lib, kw, code, msg):
     rc, err = _call(lib, _params(**kw))
     assert rc == code and msg in err, (rc, err)
+
+
+def test_fwd_accepts_the_layout_without_sfs_o(lib):
+    # a caller built against the previous layout passes its smaller size;
+    # the library then reads nothing past num_pages
+    prev = F.FmhaFwdParams.sfs_o.offset
+    rc, err = _call(lib, _params(struct_size=prev, Sq=0))
+    assert rc == F.FMHA_OK and err == ""
+    rc, err = _call(lib, _params(struct_size=prev + 4, Sq=0))
+    assert rc == F.FMHA_ERR_INVALID and "struct_size" in err
 
 
 def test_fwd_null_params(lib):

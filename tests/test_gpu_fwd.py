@@ -139,6 +139,42 @@ def test_kv_sequence_beyond_2gib():
     del kbig, vbig
 
 
+@pytest.mark.parametrize("base,S,causal", [("tiny", 200, False), ("dit", 320, False), ("dit_i8", 300, False),
+                                           ("gqa", 300, True), ("sparse", 300, False)])
+def test_e4m3_output(base, S, causal):
+    # O / sfs_o encoded to E4M3 in the epilogue; the per-head scales spread
+    # the outputs over the E4M3 range (saturation and subnormals included).
+    # Bar: each code is the encoding of a value within tol of the oracle's
+    # O, tol = the oracle's P-rounding sensitivity bound + 2^-13 (max|V| +
+    # |O|) (the accumulation error of O, whose elements can be small
+    # differences of much larger terms; a hundred times tighter than the
+    # 1.5e-2 bar of the bf16 output), and at most 1 % of the codes differ
+    # from the oracle's own encoding.
+    from oracle.attention import output_e4m3
+    from oracle.codecs import e4m3_decode
+    spec = W.small_spec(base, S, B=1, Hq=4, Hkv=2, causal=causal)
+    print(f"fwd e4m3 output {spec}", flush=True)
+    data = W.generate(spec)
+    so = np.array([2.0 ** -11, 0.004, 0.02, 1.0], dtype=np.float32)
+    _, t = Hn.gpu_run(spec, data, out_dtype="e4m3", sfs_o=torch.from_numpy(so).cuda())
+    codes = t["o"].view(torch.uint8).cpu().numpy()
+    ops = Hn.oracle_operands(spec, data)
+    ref, bound = Hn.oracle_output(spec, data, ops)
+    vmax = np.abs(ops[2]).max(axis=(0, 1, 3))[np.arange(4) // 2][None, None, :, None]
+    tol = bound + 2.0 ** -13 * (vmax + np.abs(ref))
+    got = e4m3_decode(codes)
+    lo, hi = e4m3_decode(output_e4m3(ref - tol, so)), e4m3_decode(output_e4m3(ref + tol, so))
+    ok = (got >= lo) & (got <= hi)
+    bad = [(tuple(i), float(ref[tuple(i)]), float(tol[tuple(i)]), float(got[tuple(i)] * so[i[2]]))
+           for i in np.argwhere(~ok)[:5]]
+    assert ok.all(), f"{int((~ok).sum())} codes outside the tolerance: (index, O, tol, decoded * so) {bad}"
+    want = output_e4m3(ref, so)
+    n_diff = int((e4m3_decode(want) != got).sum())
+    assert n_diff <= 0.01 * codes.size
+    assert (codes == 0x7E).any() and (((codes & 0x7F) > 0) & ((codes & 0x7F) < 8)).any()  # saturation, subnormals
+    print(f"e4m3 output {spec.name}: {n_diff} of {codes.size} codes differ from the oracle's encoding")
+
+
 def test_no_valid_key_rows_are_zero():
     import fmha_fwd_amd as F
     spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)

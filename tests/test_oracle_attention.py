@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import attention, dequantize, gather_pages
+from oracle.attention import attention, dequantize, gather_pages, output_e4m3
 from oracle.codecs import e4m3_decode
 from oracle.quantize import quantize_blocks
 
@@ -258,3 +258,21 @@ def test_rounding_sensitivity_bound_covers_tiny_score_perturbations(p_format):
         # flips are bounded by `bound`; the rescale factors move continuously
         # (relative 2^-30 of the scores, ~1e-8 here)
         assert np.all(np.abs(o2 - o) <= bound + 1e-6)
+
+
+def test_output_e4m3_hand_values():
+    # codes worked out by hand from the E4M3 definition: 448 = 1.75 * 2^8 is
+    # S.1111.110; beyond it the encoder saturates; 0.3 = 1.2 * 2^-2 rounds to
+    # 1.25 * 2^-2 (S.0101.010); 2^-10 lies half-way between 0 and the
+    # smallest subnormal 2^-9 and goes to the even code 0; 0.75 * 2^-9 rounds
+    # up to 2^-9 (S.0000.001)
+    so = np.array([0.5, 2.0])
+    vals = np.array([448.0, 500.0, -1000.0, 0.3, 2.0 ** -10, 0.75 * 2.0 ** -9, 0.0, -0.3])
+    o = np.zeros((1, len(vals), 2, 1))
+    o[0, :, 0, 0] = vals * so[0]
+    o[0, :, 1, 0] = vals * so[1]
+    want = np.array([0x7E, 0x7E, 0xFE, 0x2A, 0x00, 0x01, 0x00, 0xAA], dtype=np.uint8)
+    got = output_e4m3(o, so)
+    assert np.array_equal(got[0, :, 0, 0], want) and np.array_equal(got[0, :, 1, 0], want)
+    # no scale: the values themselves
+    assert np.array_equal(output_e4m3(o[:, :, :1] / so[0])[0, :, 0, 0], want)
