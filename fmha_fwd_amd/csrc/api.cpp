@@ -138,7 +138,9 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   const char* sn[3] = {"q", "k", "v"};
   for (int i = 0; i < 3; ++i) {
     if (sb[i] != 0 && sb[i] != 64) return fail(FMHA_ERR_UNSUPPORTED, "fwd: sage_block_%s=%d (0 or 64)", sn[i], sb[i]);
-    if (sb[i] == 64 && !sp[i]) return fail(FMHA_ERR_INVALID, "fwd: sage_block_%s=64 but sfs_%s is null", sn[i], sn[i]);
+    const bool has_blocks = i == 0 ? p->Sq > 0 : p->Skv > 0;  // an empty sequence has no scales to point at
+    if (sb[i] == 64 && !sp[i] && has_blocks)
+      return fail(FMHA_ERR_INVALID, "fwd: sage_block_%s=64 but sfs_%s is null", sn[i], sn[i]);
     if (sb[i] == 0 && sp[i]) return fail(FMHA_ERR_INVALID, "fwd: sfs_%s given but sage_block_%s=0", sn[i], sn[i]);
     if (sp[i] && reinterpret_cast<uintptr_t>(sp[i]) % 4) return fail(FMHA_ERR_INVALID, "fwd: sfs_%s misaligned", sn[i]);
   }

@@ -130,6 +130,14 @@ def test_fwd_accepts_the_layout_without_sfs_o(lib):
     assert rc == F.FMHA_ERR_INVALID and "struct_size" in err
 
 
+def test_fwd_empty_key_sequence_needs_no_scales(lib):
+    # Skv = 0: K/V and their scales may be null; every output row is zero
+    # (the launch itself needs a GPU, so only the validation is checked here:
+    # a null sfs_k with Skv > 0 is rejected, with Skv = 0 it is not)
+    rc, err = _call(lib, _params(Skv=5, sfs_v=None))
+    assert rc == F.FMHA_ERR_INVALID and "sfs_v is null" in err
+
+
 def test_fwd_null_params(lib):
     assert lib.fmha_fwd(None, None) == F.FMHA_ERR_INVALID
 

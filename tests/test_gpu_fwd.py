@@ -175,6 +175,35 @@ def test_e4m3_output(base, S, causal):
     print(f"e4m3 output {spec.name}: {n_diff} of {codes.size} codes differ from the oracle's encoding")
 
 
+@pytest.mark.parametrize("base,skv", [("dit", 100), ("gqa", 70), ("dit_i8", 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_more_queries_than_keys(base, skv, causal):
+    # Sq = 300 queries against fewer keys; bottom-right causal leaves the
+    # first Sq - Skv rows without a valid key (zero rows)
+    spec = W.small_spec(base, 300, B=1, Hq=4, Hkv=2, causal=causal)
+    print(f"fwd {spec} with Skv={skv}", flush=True)
+    data = W.generate(spec)
+    data["k"], data["v"] = data["k"][:, :skv], data["v"][:, :skv]
+    gpu, _ = Hn.gpu_run(spec, data)
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(gpu, Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data), what=f"Skv={skv}")
+    if causal:
+        assert np.all(gpu[:, :300 - skv] == 0)
+
+
+def test_no_keys_gives_zero_rows():
+    import fmha_fwd_amd as F
+    spec = W.small_spec("gqa", 130, B=1, Hq=4, Hkv=2)
+    data = W.generate(spec)
+    q, sq = F.quantize_blocks(Hn.to_gpu_bf16(data["q"]), "e4m3")
+    k = torch.zeros((1, 0, 2, 128), dtype=torch.float8_e4m3fn, device="cuda")
+    sk = torch.zeros((1, 2, 0), dtype=torch.float32, device="cuda")
+    o = torch.full((1, 130, 4, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    F.fwd(q, k, k, sfs_q=sq, sfs_k=sk, sfs_v=sk, out=o)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o) == 0
+
+
 def test_no_valid_key_rows_are_zero():
     import fmha_fwd_amd as F
     spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)
