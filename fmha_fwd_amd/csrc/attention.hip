@@ -1,5 +1,6 @@
 // Fused attention forward for gfx950: block-scaled int8 / E4M3 / bf16 Q and
-// K, E4M3 or bf16 V and P, online softmax with lazy rescaling, bf16 output.
+// K, E4M3 or bf16 V and P, online softmax with lazy rescaling, bf16 output
+// (or E4M3 with a per-head output scale).
 //
 // Method sources (FlashInfer pull-request write-ups):
 //  * #2711 page "FlashInfer의 DiT 최적화: SageAttention과 Int8/FP8 혼합 정밀도
