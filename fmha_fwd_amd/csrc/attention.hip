@@ -770,25 +770,33 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
   int buf = 0;
-  auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
-    fetch_scales(tc);
-    int tnn = n_sub;
+  // Dense two-wave instances with an E4M3 V read their V operands right after
+  // issuing the S MFMAs (32 more live registers) and issue the copies of the
+  // next sub-tile after that, in the shadow of those MFMAs; the others issue
+  // the copies first and read V in the PV step.
+  constexpr bool EARLY_V = C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED;
+  auto issue_next = [&](int& tnn) {
     if (tn < n_sub) {
       dma_k(tn, buf ^ 1, pg_n);
       dma_v(tn, buf ^ 1, pg_n);
       tnn = next_sub(tn + 1);
       if (C::PAGED && tnn < n_sub) pg_n = load_pages(tnn);
     }
-    const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
-    if constexpr (C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED) {
-      // V operands are read before the softmax so their LDS latency hides
-      // behind it (32 more live registers: two-wave dense instances only)
+  };
+  auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
+    fetch_scales(tc);
+    int tnn = n_sub;
+    if constexpr (EARLY_V) {
+      const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
       v8i vop[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + buf * C::V_BUF, d);
+      issue_next(tnn);
       __builtin_amdgcn_sched_barrier(0);
       pv_e4m3(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vop, direct_tag);
     } else {
+      issue_next(tnn);
+      const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
       pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
