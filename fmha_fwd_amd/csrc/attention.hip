@@ -484,6 +484,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
           acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].z, kr[T][j].w), q.r[2 * j + 1], acc.r[T]);
         }
       }
+    } else if constexpr (C::MT == FMT_BF16 && (C::MASKED || C::PAGED)) {
+      // masked / paged instances keep more copy state live: half the K
+      // operands (one 32-key tile) in flight at a time
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        uint4 kr[8];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) kr[tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
+        acc.r[T] = v16f{};
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[tt], acc.r[T]);
+      }
     } else if constexpr (C::MT == FMT_BF16) {
       uint4 kr[2][8];
 #pragma unroll

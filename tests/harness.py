@@ -85,7 +85,7 @@ def gpu_run(spec, data, device="cuda", **fwd_kw):
         n_pages = pt.numel()
         S = spec.S
         kpool = torch.zeros((n_pages, ps) + tuple(k.shape[2:]), dtype=k.dtype, device=device)
-        vpool = torch.zeros_like(kpool)
+        vpool = torch.zeros((n_pages, ps) + tuple(v.shape[2:]), dtype=v.dtype, device=device)
         for b in range(spec.B):
             for p in range(pt.shape[1]):
                 lo, hi = p * ps, min(p * ps + ps, S)

@@ -56,6 +56,13 @@ def test_small_sparse_contiguous(S):
     _run_small(W.small_spec("sparse", S, B=1, Hq=2, Hkv=2, paged=False))
 
 
+@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8", "gqa"])
+@pytest.mark.parametrize("masked,paged", [(True, False), (False, True), (True, True)])
+def test_other_formats_masked_or_paged(base, masked, paged):
+    # the block-sparse and paged paths for the other four format combinations
+    _run_small(W.small_spec(base, 300, B=2, Hq=4, Hkv=2, masked=masked, paged=paged))
+
+
 def test_small_paged_dense():
     _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=1, masked=False))
 
