@@ -209,6 +209,7 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   a.mask = p->block_mask;
   a.m_sb = p->mask_stride_b; a.m_sh = p->mask_stride_h; a.m_sqb = p->mask_stride_qb;
   a.mask_kv_sub = p->block_mask ? p->mask_block_kv / 64 : 1;
+  a.mask_kv_shift = (a.mask_kv_sub & (a.mask_kv_sub - 1)) == 0 ? __builtin_ctz((unsigned)a.mask_kv_sub) : -1;
   a.page_table = p->page_table;
   a.pt_sb = p->page_table_stride_b;
   a.page_size = paged ? p->page_size : 1;

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   auto next_sub = [&](int t) {
     if constexpr (C::MASKED) {
       if (t >= n_sub) return n_sub;
-      int mb = t / kvsub;
+      int mb = a.mask_kv_shift >= 0 ? t >> a.mask_kv_shift : t / kvsub;
       while (mb * kvsub < n_sub) {
         if (mb - mb_base >= 64) {
           mb_base = mb;
@@ -284,11 +284,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
   }
   // Page numbers of sub-tile t: entry i of the sub-tile in lane i (i < 4).
+  // The table entry is checked where it is used (page_addr), a sub-tile
+  // later: a check here would wait for this load and every copy before it.
   auto load_pages = [&](int t) {
     if constexpr (!C::PAGED) return 0;
     const int first = (t * kSub) >> page_shift, last = (a.Skv - 1) >> page_shift;
-    int page = pt_row[min(first + (lane & 3), last)];
-    return (unsigned)page < (unsigned)a.num_pages ? page : 0;  // outside the pool: page 0
+    return pt_row[min(first + (lane & 3), last)];
   };
   auto tile_rsrc = [&](const uint8_t* base, int64_t ss, int kv0) {
     const uint64_t rem = (uint64_t)(a.Skv - kv0) * (uint64_t)ss;
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // slot lane & 3, whose page number this lane holds; one 64-bit product per
   // sub-tile and tensor, shared by every copy through ds_bpermute.
   auto page_addr = [&](const uint8_t* base, int64_t sb, int64_t ss, int kv0, int page) {
+    page = (unsigned)page < (unsigned)a.num_pages ? page : 0;  // outside the pool: page 0
     const int64_t in_page = (int64_t)(kv0 & (a.page_size - 1)) * ss;  // pages longer than a sub-tile
     return (uint64_t)(base + in_page) + (uint64_t)(uint32_t)page * (uint64_t)sb;
   };

@@ -37,6 +37,7 @@ struct FwdArgs {
   const uint8_t* mask;  // null = dense
   int64_t m_sb, m_sh, m_sqb;
   int mask_kv_sub;      // 64-key sub-tiles per mask key block
+  int mask_kv_shift;    // log2(mask_kv_sub) when it is a power of two, else -1
   const int32_t* page_table;  // null = contiguous
   int64_t pt_sb;
   int page_size, num_pages;
