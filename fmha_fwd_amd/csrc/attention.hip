@@ -71,6 +71,15 @@ __device__ __forceinline__ int sigma(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
+// A register of no particular value (no instruction): the low half of a
+// packed P word is written first and the high half second, so the initial
+// contents never reach a result.
+__device__ __forceinline__ int any_vgpr() {
+  int v;
+  asm volatile("" : "=v"(v));
+  return v;
+}
+
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -679,7 +688,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       if constexpr (C::VF == FMT_E4M3) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
-          int pk = pack_e4m3<false>(st.s[4 * w], st.s[4 * w + 1], 0);
+          int pk = pack_e4m3<false>(st.s[4 * w], st.s[4 * w + 1], any_vgpr());
           pk = pack_e4m3<true>(st.s[4 * w + 2], st.s[4 * w + 3], pk);
           st.pt.pb[w] = pk;
         }
