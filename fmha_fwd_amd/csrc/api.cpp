@@ -214,6 +214,10 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   a.pt_sb = p->page_table_stride_b;
   a.page_size = paged ? p->page_size : 1;
   a.num_pages = paged ? p->num_pages : 0;
+  // every offset inside a pool is below num_pages * page stride (a page holds
+  // its page_size slots): 32-bit page offsets when that is under 4 GiB
+  a.pool32 = paged && (int64_t)p->num_pages * std::max(a.k_sb, a.v_sb) < ((int64_t)1 << 32) &&
+             (int64_t)p->page_size * std::max(a.k_ss, a.v_ss) <= std::max(a.k_sb, a.v_sb);
   // P <= 2^tau / sfs_p; E4M3 conversion needs a clamp once that can reach 464.
   a.clamp_p = (p->sfs_p != nullptr) || (p->lazy_rescale_log2 > 8.5f);
   // Contiguous K/V: with positive token strides and a sequence (plus one

@@ -333,6 +333,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(ps << 2, (int)(uint32_t)(pa >> 32));
     return (const uint8_t*)((((uint64_t)hi << 32) | lo) + off);
   };
+  // Pools under 4 GiB: the page offset from the pool base fits 32 bits, so
+  // a copy needs one exchange and its address is the (scalar) base plus a
+  // 32-bit offset (instances with at most five copies per tensor and wave;
+  // the second code path costs the others spills).
+  constexpr bool P32 = KSL <= 5 && VSL <= 5;
+  auto page_off32 = [&](int64_t sb, int64_t ss, int kv0, int page) {
+    page = (unsigned)page < (unsigned)a.num_pages ? page : 0;  // outside the pool: page 0
+    return (uint32_t)page * (uint32_t)sb + (uint32_t)((kv0 & (a.page_size - 1)) * ss);
+  };
+  auto paged_off32 = [&](uint32_t po, int idx, uint32_t off) {
+    const int ps = (int)(pslot_bits >> (2 * idx)) & 3;
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(ps << 2, (int)po) + off;
+  };
   auto dma_k = [&](int t, int buf, int pages) {
     const int kv0 = t * kSub;
     lds_u8* dst = kbuf0 + buf * C::K_BUF;
@@ -344,6 +357,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         const int j = wave + sl * C::NW;
         if (C::K_DMA_OPS % C::NW == 0 || sl + 1 < KSL || j < C::K_DMA_OPS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)k_src[sl], soff, 0, 0);
+      }
+    } else if (P32 && kv0 + kSub <= a.Skv && a.pool32) {
+      const uint32_t po = page_off32(a.k_sb, a.k_ss, kv0, pages);
+      uint32_t off[KSL];
+#pragma unroll
+      for (int sl = 0; sl < KSL; ++sl) off[sl] = paged_off32(po, sl, k_src[sl]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sl = 0; sl < KSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::K_DMA_OPS - 1);
+        __builtin_amdgcn_global_load_lds(kbase + off[sl], FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
       // all page exchanges first, so their latencies overlap
@@ -381,6 +405,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         const int j = wave + sl * C::NW;
         if (C::V_DMA_OPS % C::NW == 0 || sl + 1 < VSL || j < C::V_DMA_OPS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FMHA_LDS(void, dst + j * 1024), 16, (int)v_src[sl], soff, 0, 0);
+      }
+    } else if (P32 && kv0 + kSub <= a.Skv && a.pool32) {
+      const uint32_t po = page_off32(a.v_sb, a.v_ss, kv0, pages);
+      uint32_t off[VSL];
+#pragma unroll
+      for (int sl = 0; sl < VSL; ++sl) off[sl] = paged_off32(po, KSL + sl, v_src[sl]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sl = 0; sl < VSL; ++sl) {
+        const int j = min(wave + sl * C::NW, C::V_DMA_OPS - 1);
+        __builtin_amdgcn_global_load_lds(vbase + off[sl], FMHA_LDS(void, dst + j * 1024), 16, 0, 0);
       }
     } else if (kv0 + kSub <= a.Skv) {
       const uint64_t pa = page_addr(vbase, a.v_sb, a.v_ss, kv0, pages);

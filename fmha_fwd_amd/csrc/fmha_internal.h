@@ -41,6 +41,7 @@ struct FwdArgs {
   const int32_t* page_table;  // null = contiguous
   int64_t pt_sb;
   int page_size, num_pages;
+  int pool32;           // paged K/V pools span < 4 GiB from their (head-offset) base
   const float* sfs_p;   // [Hq] or null
   int clamp_p;          // P / sp may reach the E4M3 overflow range
   int pack_heads;       // set by the launcher: a workgroup takes 32 queries of NW heads sharing a KV head

@@ -211,6 +211,37 @@ def test_no_keys_gives_zero_rows():
     assert torch.count_nonzero(o) == 0
 
 
+def test_paged_pool_beyond_4gib():
+    # pages 256 MiB apart: the pool spans more than 2^32 bytes, so the copies
+    # take 64-bit page addresses instead of 32-bit offsets from the pool base
+    import fmha_fwd_amd as F
+    spec = W.small_spec("sparse", 300, B=1, Hq=2, Hkv=2)
+    print(f"fwd {spec} with a pool of 256 MiB page stride", flush=True)
+    data = W.generate(spec)
+    pt = data["page_table"]                       # [1, 19] pool pages 0..18
+    n_pages, ps = pt.size, spec.page_size
+    q = Hn.to_gpu_bf16(data["q"])
+    kc, sk = F.quantize_blocks(Hn.to_gpu_bf16(data["k"]), "e4m3")
+    vc, sv = F.quantize_blocks(Hn.to_gpu_bf16(data["v"]), "e4m3")
+    stride = 1 << 28
+    assert n_pages * stride >= 1 << 32
+    pools = []
+    for codes in (kc, vc):
+        big = torch.empty(n_pages * stride, dtype=torch.uint8, device="cuda")
+        pool = big.as_strided((n_pages, ps, 2, 128), (stride, 256, 128, 1))
+        padded = torch.zeros((n_pages * ps, 2, 128), dtype=torch.uint8, device="cuda")
+        padded[:300] = codes.view(torch.uint8)[0]
+        pool[torch.from_numpy(pt.reshape(-1)).long().cuda()] = padded.view(n_pages, ps, 2, 128)
+        pools.append((big, pool.view(torch.float8_e4m3fn)))
+    o = F.fwd(q, pools[0][1], pools[1][1], sfs_k=sk, sfs_v=sv, block_mask=torch.from_numpy(data["block_mask"]).cuda(),
+              page_table=torch.from_numpy(pt).cuda(), page_size=ps, seq_len_kv=300)
+    torch.cuda.synchronize()
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(o.float().cpu().numpy(), Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data),
+                     what="pool beyond 4 GiB")
+    del pools
+
+
 def test_no_valid_key_rows_are_zero():
     import fmha_fwd_amd as F
     spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)
