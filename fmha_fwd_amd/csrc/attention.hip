@@ -60,6 +60,9 @@ constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per 
 #ifndef FMHA_WAVES_PER_EU_BF16
 #define FMHA_WAVES_PER_EU_BF16 2
 #endif
+#ifndef FMHA_ROW_PACK
+#define FMHA_ROW_PACK 1  // 0: at most one head per wave
+#endif
 #ifndef FMHA_HEAD_PACK
 #define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
 #endif
@@ -89,12 +92,16 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_>
+template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_,
+          bool RP_ = false>
 struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
+  // RP: heads packed inside a wave (fewer than 32 rows per head), so a
+  // lane's head, Q scale and P scale are its own (two more live registers)
+  static constexpr bool RP = RP_;
   static constexpr int MT = QF;                                  // QK operand format
-  static constexpr int WPE = MT == FMT_BF16 || MASKED || PAGED ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
+  static constexpr int WPE = MT == FMT_BF16 || MASKED || PAGED || RP ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
@@ -150,30 +157,43 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 
   // ---- which (batch, head, query tile) this workgroup owns
   // Either NW x 32 consecutive queries of one head, or (head packing, for
-  // grouped-query attention with short or causal query ranges) the same 32
-  // queries of NW query heads that share one KV head: every wave then needs
-  // the same keys and K/V tiles serve NW heads at once.
-  const bool pack = !C::MASKED && a.pack_heads;
-  const int qtile = pack ? 32 : 32 * C::NW;
+  // grouped-query attention with short or causal query ranges) the same R
+  // queries of NW * 32 / R query heads that share one KV head, R / 32 of a
+  // wave's rows per head: every row then needs the same keys, and K/V tiles
+  // serve all those heads at once.  Rows are independent, so a lane's head
+  // and query only change where its row is loaded, scaled and stored.
+  const int rows = C::MASKED || !a.pack_rows ? 0 : (C::RP ? a.pack_rows : 32);  // R (0: no packing)
+  const bool pack = rows > 0;
+  const int qtile = pack ? rows : 32 * C::NW;
   const int nqt = (a.Sq + qtile - 1) / qtile;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   int qt = lin % nqt;
   if (a.causal) qt = nqt - 1 - qt;  // longest causal rows first
   const int rest = lin / nqt;
-  int hq, b;
-  if (pack) {
-    const int gpw = a.group / C::NW;  // workgroups per KV head and query tile
+  int hq, b, hk;
+  int qi;  // this lane's query row
+  if (C::RP) {
+    const int hpw = 32 / rows;                 // heads per wave
+    const int gpw = a.group / (C::NW * hpw);   // workgroups per KV head and query tile
     const int bhk = rest / gpw;
-    hq = (bhk % a.Hkv) * a.group + (rest % gpw) * C::NW + wave;
+    hk = bhk % a.Hkv;
+    hq = hk * a.group + (rest % gpw) * (C::NW * hpw) + wave * hpw + m32 / rows;
     b = bhk / a.Hkv;
+    qi = qt * qtile + m32 % rows;
+  } else if (pack) {
+    const int gpw = a.group / C::NW;
+    const int bhk = rest / gpw;
+    hk = bhk % a.Hkv;
+    hq = hk * a.group + (rest % gpw) * C::NW + wave;
+    b = bhk / a.Hkv;
+    qi = qt * qtile + m32;
   } else {
     hq = rest % a.Hq;
     b = rest / a.Hq;
+    hk = hq / a.group;
+    qi = qt * qtile + 32 * wave + m32;
   }
-  const int hk = hq / a.group;
   const int q0 = qt * qtile;
-  const int q0w = pack ? q0 : q0 + 32 * wave;
-  const int qi = q0w + m32;                // this lane's query row
   const int causal_off = a.Skv - a.Sq;     // key j visible iff j <= i + causal_off
 
   // ---- key range of the workgroup; sub-tiles needing per-pair masks
@@ -468,7 +488,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
   }
   float sq = 1.0f;
-  if (C::QS) sq = a.sfs_q[((int64_t)b * a.Hq + hq) * a.nblk_q + min(q0w, max(a.Sq - 1, 0)) / 64];
+  if (C::QS) {
+    const int qs = C::RP ? qi : (pack ? q0 : q0 + 32 * wave);  // wave-uniform unless rows hold several heads
+    sq = a.sfs_q[((int64_t)b * a.Hq + hq) * a.nblk_q + min(qs, max(a.Sq - 1, 0)) / 64];
+  }
   const float log2sp = a.sfs_p ? __log2f(a.sfs_p[hq]) : 0.0f;
   const float* sk_row = C::KS ? a.sfs_k + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
   const float* sv_row = C::VS ? a.sfs_v + ((int64_t)b * a.Hkv + hk) * a.nblk_kv : nullptr;
@@ -923,15 +946,30 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 #endif
 }
 
+// Rows per head of a packed workgroup (0: no packing).  Heads are packed
+// when the query range is causal or shorter than a workgroup tile; query
+// ranges shorter than 16 also pack heads inside a wave: R rows per head, R
+// the smallest power of two >= Sq that the group size still allows.
+int pack_rows(const FwdArgs& a, int nw) {
+  const bool pack = FMHA_HEAD_PACK && a.mask == nullptr && a.group % nw == 0 && (a.causal || a.Sq < 32 * nw);
+  if (!pack) return 0;
+  int rows = 32;
+  while (FMHA_ROW_PACK && rows > 1 && rows / 2 >= a.Sq && (a.group / nw) % (64 / rows) == 0) rows /= 2;
+  return rows;
+}
+
 template <class C>
 hipError_t launch(const FwdArgs& args, hipStream_t stream) {
   // Head packing where K/V reuse across the heads of a group pays: a query
   // range shorter than one workgroup tile, or a causal one (the waves then
   // share one diagonal instead of staggering along it).
   FwdArgs a = args;
-  a.pack_heads = FMHA_HEAD_PACK && !C::MASKED && a.group % C::NW == 0 && (a.causal || a.Sq < 32 * C::NW);
-  const int qtile = a.pack_heads ? 32 : 32 * C::NW;
-  const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B / (a.pack_heads ? C::NW : 1);
+  a.pack_rows = pack_rows(a, C::NW);
+  if (!C::RP && a.pack_rows) a.pack_rows = 32;
+  const bool pack = a.pack_rows > 0;
+  const int rows = pack ? a.pack_rows : 32;
+  const int qtile = pack ? rows : 32 * C::NW;
+  const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B / (pack ? C::NW * (32 / rows) : 1);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles);
   const size_t lds = (size_t)C::LDS_BYTES;
@@ -962,6 +1000,11 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
   if (k.masked) {
     if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, true, true, 2>>(a, s);
     return launch<Cfg<QF, KF, VF, QS, KS, VS, true, false, 2>>(a, s);
+  }
+  const int rows = pack_rows(a, kDenseWaves);
+  if (rows > 0 && rows < 32) {
+    if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves, true>>(a, s);
+    return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves, true>>(a, s);
   }
   if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves>>(a, s);
   return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves>>(a, s);

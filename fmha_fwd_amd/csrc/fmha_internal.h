@@ -44,7 +44,7 @@ struct FwdArgs {
   int pool32;           // paged K/V pools span < 4 GiB from their (head-offset) base
   const float* sfs_p;   // [Hq] or null
   int clamp_p;          // P / sp may reach the E4M3 overflow range
-  int pack_heads;       // set by the launcher: a workgroup takes 32 queries of NW heads sharing a KV head
+  int pack_rows;        // set by the launcher: 0, or R: a workgroup takes R queries of NW * 32 / R heads sharing a KV head
   int kv_whole_rsrc;    // contiguous K/V of one (batch, head) span < 2^31 bytes: one buffer resource each
   int o_fp8;            // o is E4M3: encode(O / sfs_o[h])
   const float* sfs_o;   // [Hq] or null (= 1)

@@ -82,6 +82,8 @@ SPECS = {
     "sparse": Spec("sparse", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True, paged=True),
     # a prefill chunk: the last 256 positions of the gqa sequence against all of its keys
     "gqa_chunk": Spec("gqa_chunk", 5, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=256),
+    # 16 new positions per sequence (a short prefill step) for 64 sequences
+    "gqa_step": Spec("gqa_step", 6, 64, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=16),
 }
 
 

@@ -282,6 +282,15 @@ def test_query_chunk_gqa(sq, S, causal):
     _run_small(W.small_spec("gqa", S, B=1, Hq=8, Hkv=2, causal=causal, sq=sq))
 
 
+@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "tiny", "sparse"])
+@pytest.mark.parametrize("hq,sq", [(16, 1), (16, 5), (16, 16), (32, 3), (32, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_several_heads_per_wave(base, hq, sq, causal):
+    # query chunks shorter than 16 with 8 or 16 query heads per KV head: a
+    # wave's 32 rows hold 2 or 4 heads (16 or 8 rows each)
+    _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=causal, sq=sq, masked=False))
+
+
 @pytest.mark.parametrize("S", [1, 130, 320])
 def test_small_causal_gqa_packed(S):
     _run_small(W.small_spec("gqa", S, B=2, Hq=8, Hkv=2, causal=True))
