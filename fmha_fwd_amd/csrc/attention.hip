@@ -838,8 +838,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // sub-tile a wave runs S^T = K Q^T (MFMA), the softmax (VALU), then
   // O^T += V^T P^T (MFMA); MFMA/VALU overlap comes from the other wave on the
   // SIMD being in another phase.  The copies of the next sub-tile are issued
-  // first and land while the current one is processed (paged: its page
-  // numbers were read during the previous sub-tile).
+  // early in the step and land while the current one is processed (paged:
+  // its page numbers were read during the previous sub-tile).
   int tc = next_sub(0);
   int tn = n_sub, pg_n = 0;
   if (tc < n_sub) {
