@@ -283,11 +283,11 @@ def test_query_chunk_gqa(sq, S, causal):
 
 
 @pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "tiny", "sparse"])
-@pytest.mark.parametrize("hq,sq", [(16, 1), (16, 5), (16, 16), (32, 3), (32, 8)])
+@pytest.mark.parametrize("hq,sq", [(16, 1), (16, 5), (16, 16), (32, 3), (32, 8), (64, 1), (64, 4)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rows_of_several_heads_per_wave(base, hq, sq, causal):
-    # query chunks shorter than 16 with 8 or 16 query heads per KV head: a
-    # wave's 32 rows hold 2 or 4 heads (16 or 8 rows each)
+    # query chunks shorter than 16 with 8, 16 or 32 query heads per KV head:
+    # a wave's 32 rows hold 2, 4 or 8 heads (16, 8 or 4 rows each)
     _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=causal, sq=sq, masked=False))
 
 
