@@ -242,6 +242,21 @@ def test_paged_pool_beyond_4gib():
     del pools
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_block_mask_broadcast_over_batch_and_heads(paged):
+    # one [q_blocks, kv_blocks] mask expanded to [B, Hq, ...] (strides 0)
+    spec = W.small_spec("sparse", 700, B=2, Hq=4, Hkv=2, paged=paged)
+    print(f"fwd {spec} with a broadcast mask", flush=True)
+    data = W.generate(spec)
+    one = data["block_mask"][0, 0]
+    data["block_mask"] = np.broadcast_to(one, data["block_mask"].shape).copy()
+    mask = torch.from_numpy(one.copy()).cuda().expand(2, 4, *one.shape)
+    assert mask.stride(0) == 0 and mask.stride(1) == 0
+    gpu, _ = Hn.gpu_run(spec, data, block_mask=mask)
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(gpu, Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data), what="broadcast mask")
+
+
 def test_no_valid_key_rows_are_zero():
     import fmha_fwd_amd as F
     spec = W.small_spec("sparse", 256, B=1, Hq=1, Hkv=1, paged=False)
