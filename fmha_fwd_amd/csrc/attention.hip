@@ -851,47 +851,66 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
-  int buf = 0;
   // Dense two-wave instances with an E4M3 V read their V operands right after
   // issuing the S MFMAs (32 more live registers) and issue the copies of the
   // next sub-tile after that, in the shadow of those MFMAs; the others issue
   // the copies first and read V in the PV step.
   constexpr bool EARLY_V = C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED;
-  auto issue_next = [&](int& tnn) {
+  // The buffer holding sub-tile tc: the captured `buf`, toggled by each
+  // step, or (unrolled dense loop) a compile-time 0 / 1, so that LDS
+  // addresses fold into the instructions.
+  int buf = 0;
+  auto issue_next = [&](int& tnn, int bv) {
     if (tn < n_sub) {
-      dma_k(tn, buf ^ 1, pg_n);
-      dma_v(tn, buf ^ 1, pg_n);
+      dma_k(tn, bv ^ 1, pg_n);
+      dma_v(tn, bv ^ 1, pg_n);
       tnn = next_sub(tn + 1);
       if (C::PAGED && tnn < n_sub) pg_n = load_pages(tnn);
     }
   };
-  auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag) {
+  auto step = [&](auto edge_tag, auto clamp_tag, auto direct_tag, auto buf_tag) {
+    constexpr int FIXED = decltype(buf_tag)::value;  // -1: the captured buf
+    const int bv = FIXED >= 0 ? FIXED : buf;
     fetch_scales(tc);
     int tnn = n_sub;
     if constexpr (EARLY_V) {
-      const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
+      const SAcc<C::MT> acc = qk(kbuf0 + bv * C::K_BUF, std::true_type{});
       v8i vop[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + buf * C::V_BUF, d);
-      issue_next(tnn);
+      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + bv * C::V_BUF, d);
+      issue_next(tnn, bv);
       __builtin_amdgcn_sched_barrier(0);
       pv_e4m3(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vop, direct_tag);
     } else {
-      issue_next(tnn);
-      const SAcc<C::MT> acc = qk(kbuf0 + buf * C::K_BUF, std::true_type{});
-      pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + buf * C::V_BUF, direct_tag);
+      issue_next(tnn, bv);
+      const SAcc<C::MT> acc = qk(kbuf0 + bv * C::K_BUF, std::true_type{});
+      pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + bv * C::V_BUF, direct_tag);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
-    buf ^= 1;
+    if (FIXED < 0) buf ^= 1;
     tc = tn;
     tn = tnn;
   };
+  using BufRt = std::integral_constant<int, -1>;
   auto run = [&](auto clamp_tag, auto direct_tag) {
     // sub-tiles valid for every pair of the workgroup first (a block mask
-    // only skips whole sub-tiles), then the edge ones
-    while (tc < n_sub && tc < full_end) step(std::false_type{}, clamp_tag, direct_tag);
-    while (tc < n_sub) step(std::true_type{}, clamp_tag, direct_tag);
+    // only skips whole sub-tiles), then the edge ones; dense contiguous
+    // instances take the first kind two per trip with the buffers fixed (the
+    // others have no registers to spare for the longer loop)
+    if constexpr (!C::MASKED && !C::PAGED) {
+      while (tc < n_sub && tc < full_end) {
+        [[clang::always_inline]] step(std::false_type{}, clamp_tag, direct_tag, std::integral_constant<int, 0>{});
+        if (!(tc < n_sub && tc < full_end)) {
+          buf = 1;
+          break;
+        }
+        [[clang::always_inline]] step(std::false_type{}, clamp_tag, direct_tag, std::integral_constant<int, 1>{});
+      }
+    } else {
+      while (tc < n_sub && tc < full_end) step(std::false_type{}, clamp_tag, direct_tag, BufRt{});
+    }
+    while (tc < n_sub) step(std::true_type{}, clamp_tag, direct_tag, BufRt{});
   };
   const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;
   if constexpr (C::VS) {
