@@ -63,6 +63,9 @@ constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per 
 #ifndef FMHA_ROW_PACK
 #define FMHA_ROW_PACK 1  // 0: at most one head per wave
 #endif
+#ifndef FMHA_ROW_PACK_NW2
+#define FMHA_ROW_PACK_NW2 1  // 0: no two-wave workgroups for small groups
+#endif
 #ifndef FMHA_HEAD_PACK
 #define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
 #endif
@@ -1024,6 +1027,16 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
   if (rows > 0 && rows < 32) {
     if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves, true>>(a, s);
     return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves, true>>(a, s);
+  }
+  // Groups too small to fill four waves with several heads each (e.g. four
+  // query heads per KV head) use two-wave workgroups; with 8-bit K in LDS
+  // four of them still fit a CU.
+  if constexpr (KF != FMT_BF16) {
+    const int rows2 = pack_rows(a, 2);
+    if (FMHA_ROW_PACK_NW2 && rows2 > 0 && rows2 < 32) {
+      if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, 2, true>>(a, s);
+      return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, 2, true>>(a, s);
+    }
   }
   if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves>>(a, s);
   return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves>>(a, s);

@@ -84,6 +84,8 @@ SPECS = {
     "gqa_chunk": Spec("gqa_chunk", 5, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=256),
     # 16 new positions per sequence (a short prefill step) for 64 sequences
     "gqa_step": Spec("gqa_step", 6, 64, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=16),
+    # the same step with four query heads per KV head (32 / 8)
+    "gqa4_step": Spec("gqa4_step", 7, 64, 32, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=16),
 }
 
 

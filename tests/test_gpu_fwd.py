@@ -306,6 +306,15 @@ def test_rows_of_several_heads_per_wave(base, hq, sq, causal):
     _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=causal, sq=sq, masked=False))
 
 
+@pytest.mark.parametrize("base", ["gqa", "dit_i8", "sparse"])
+@pytest.mark.parametrize("sq", [1, 7, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_two_heads_in_two_wave_workgroups(base, sq, causal):
+    # four query heads per KV head: two-wave workgroups of two heads per wave
+    # (8-bit K formats)
+    _run_small(W.small_spec(base, 300, B=2, Hq=8, Hkv=2, causal=causal, sq=sq, masked=False))
+
+
 @pytest.mark.parametrize("S", [1, 130, 320])
 def test_small_causal_gqa_packed(S):
     _run_small(W.small_spec("gqa", S, B=2, Hq=8, Hkv=2, causal=True))
