@@ -619,6 +619,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     return acc;
   };
 
+  // S^T with the wave's issue priority raised while its MFMAs are issued:
+  // the other wave on the SIMD is then usually in its softmax, and the
+  // matrix core gets its next block sooner (+1.5-2 % measured).
+  auto qk_raised = [&](const lds_u8* kb) {
+    __builtin_amdgcn_s_setprio(1);
+    const SAcc<C::MT> acc = qk(kb, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    return acc;
+  };
+
   // ---- per-lane state.  O^T (4 tiles of 32 d x 32 queries) is kept in units
   // of the reference V scale `sv_ref`: before a sub-tile's PV product is
   // accumulated, O is multiplied by alpha_row * sv_ref / sv_tile (one multiply
@@ -877,7 +888,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     fetch_scales(tc);
     int tnn = n_sub;
     if constexpr (EARLY_V) {
-      const SAcc<C::MT> acc = qk(kbuf0 + bv * C::K_BUF, std::true_type{});
+      const SAcc<C::MT> acc = qk_raised(kbuf0 + bv * C::K_BUF);
       v8i vop[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + bv * C::V_BUF, d);
@@ -886,7 +897,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       pv_e4m3(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vop, direct_tag);
     } else {
       issue_next(tnn, bv);
-      const SAcc<C::MT> acc = qk(kbuf0 + bv * C::K_BUF, std::true_type{});
+      const SAcc<C::MT> acc = qk_raised(kbuf0 + bv * C::K_BUF);
       pv(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vbuf0 + bv * C::V_BUF, direct_tag);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
