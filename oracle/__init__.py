@@ -16,14 +16,18 @@ cited below by PR number, section and, where useful, bullet):
 * #4474 page -- "FlashInfer의 PrimTS를 활용한 고성능 Block-Sparse Attention
   최적화" (Q64xKV256 profile, block-sparse attention over contiguous or paged
   K/V).
+* #3237 page -- "FlashInfer의 Per-token NVFP4 Quantization 커널 최적화 분석"
+  (per-token NVFP4 quantisation of activations).
 
 Modules:
   codecs     -- bf16 / OCP-E4M3 / int8 encoders and decoders (closed form).
   quantize   -- per-(batch, head, 64-token block) quantisation.
   attention  -- attention over dequantised tensors, emulating P quantisation
                 and the lazy rescale; also exact and unquantised variants.
+  nvfp4      -- per-token NVFP4 (E2M1 elements, E4M3 16-element block scales,
+                fp32 token scale) quantisation.
 
 Every function states the passage it follows; where the pages are silent the
 reading taken is stated at the point of use.
 """
-from . import codecs, quantize, attention  # noqa: F401
+from . import codecs, quantize, attention, nvfp4  # noqa: F401
