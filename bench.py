@@ -11,6 +11,9 @@ two device synchronisations; per-kernel durations come from HIP events
 recorded on the launch stream around every launch of the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--workload dit] [--no-cpu-baseline]
+
+`--workload nvfp4` measures the per-token NVFP4 quantiser instead (GB/s
+against the HBM peak; one step = one launch over a 16384 x 8192 matrix).
 """
 import argparse
 import hashlib
@@ -109,6 +112,98 @@ def cpu_baseline(spec, data, budget_s=12.0):
 
 
 COPY_BYTES = 1 << 30
+NVFP4_METRIC = "per-token NVFP4 quantisation GB/s (algorithmic bytes: 2 read + 0.5 + 1/16 written per element, 4 per token)"
+
+
+def nvfp4_bytes(M, K):
+    return M * K * 2 + M * K // 2 + M * K // 16 + 4 * M
+
+
+def nvfp4_source_hash():
+    h = hashlib.sha256()
+    for f in ("nvfp4.hip", "device_common.h"):
+        h.update(open(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def nvfp4_cpu_baseline(x_rows_fn, M, K, budget_s=12.0):
+    """The NVFP4 oracle (as it stands) on a bounded row sample."""
+    from oracle.nvfp4 import quantize_nvfp4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rng = np.random.default_rng(0)
+    rows_done, t = 0, 0.0
+    while t < budget_s and rows_done < M:
+        g = int(rng.integers(0, max(M // 256, 1)))
+        x = x_rows_fn(np.arange(256 * g, min(256 * g + 256, M)))  # one 256-row group
+        t0 = time.perf_counter()
+        quantize_nvfp4(x)
+        t += time.perf_counter() - t0
+        rows_done += 256
+    return {"value": nvfp4_bytes(rows_done, K) / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "rows_per_s": rows_done / t, "extrapolated_full_s": M / (rows_done / t),
+            "sample": f"{rows_done} rows (random 256-row groups) of the {M} x {K} matrix, NVFP4 oracle in numpy float32 emulation; "
+                      f"{t:.1f} s of CPU time", "seconds": round(t, 2)}
+
+
+def bench_nvfp4(args, torch, F, W):
+    """One step = one fmha_quantize_nvfp4 launch over the whole matrix."""
+    idx, M, K = W.NVFP4_SPECS[args.workload]
+    x_host = W.nvfp4_activations(M, K, idx)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    F.lib_handle()
+    x = torch.from_numpy(x_host).to(torch.bfloat16).to(dev)
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((M, K // 16), dtype=torch.float8_e4m3fn, device=dev)
+    ts = torch.empty((M,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        F.quantize_nvfp4(x, codes=codes, block_scales=sf, token_scales=ts, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ms_step = wall * 1e3 / args.steps
+    nbytes = nvfp4_bytes(M, K)
+    achieved = nbytes / (np.mean(k_ms) * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"{args.workload}_traffic.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_hash") == nvfp4_source_hash():
+            traffic = t.get("bytes_per_launch")
+    rec = {
+        "metric": NVFP4_METRIC,
+        "value": nbytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16-in/e2m1-e4m3-out", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "quantize_nvfp4"},
+        "kernel_ms": float(np.mean(k_ms)), "kernel_ms_min": float(np.min(k_ms)),
+        "hbm_copy_gbs": copy_bandwidth(torch),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = nvfp4_cpu_baseline(lambda r: W.nvfp4_activations(M, K, idx, rows=r), M, K)
+    print(json.dumps(rec), flush=True)
 
 
 def copy_bandwidth(torch, reps=5):
@@ -163,6 +258,9 @@ def main():
     import fmha_fwd_amd as F
     from fmha_fwd_amd import workloads as W
 
+    if args.workload in W.NVFP4_SPECS:
+        bench_nvfp4(args, torch, F, W)
+        return
     spec = W.SPECS[args.workload]
     data = W.generate(spec)
     dev = torch.device("cuda:0")

@@ -7,6 +7,7 @@ missing, importing ``fmha_fwd_amd.lib_handle()`` raises.
 
     codes, scales = quantize_blocks(x, "e4m3")           # x: bf16 [B,S,H,128]
     o = fwd(q, k, v, sfs_q=..., sfs_k=..., sfs_v=..., causal=True)
+    codes, block_scales, token_scales = quantize_nvfp4(a)  # a: bf16 [M, K]
 """
 import ctypes
 import math
@@ -17,7 +18,7 @@ LIB_PATH = os.environ.get("FMHA_LIB") or os.path.join(os.path.dirname(os.path.ab
 
 FMHA_DT_BF16, FMHA_DT_E4M3, FMHA_DT_INT8 = 1, 2, 3
 FMHA_OK, FMHA_ERR_INVALID, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP = 0, -1, -2, -3
-EXPORTED = ("fmha_quantize_blocks", "fmha_fwd", "fmha_last_error", "fmha_abi_version")
+EXPORTED = ("fmha_quantize_blocks", "fmha_fwd", "fmha_quantize_nvfp4", "fmha_last_error", "fmha_abi_version")
 
 
 class FmhaTensor(ctypes.Structure):
@@ -70,6 +71,10 @@ def lib_handle():
         lib.fmha_quantize_blocks.restype = ctypes.c_int
         lib.fmha_fwd.argtypes = [ctypes.POINTER(FmhaFwdParams), ctypes.c_void_p]
         lib.fmha_fwd.restype = ctypes.c_int
+        lib.fmha_quantize_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        lib.fmha_quantize_nvfp4.restype = ctypes.c_int
         lib.fmha_last_error.argtypes = []
         lib.fmha_last_error.restype = ctypes.c_char_p
         lib.fmha_abi_version.argtypes = []
@@ -135,6 +140,36 @@ def quantize_blocks(x, dtype="e4m3", *, codes=None, scales=None, stream=None):
     _check(lib_handle().fmha_quantize_blocks(ctypes.byref(xt), ctypes.byref(ct), scales.data_ptr(),
                                              B, S, H, D, 64, _stream(stream)))
     return codes, scales
+
+
+def quantize_nvfp4(x, *, codes=None, block_scales=None, token_scales=None, stream=None):
+    """Per-token NVFP4 quantisation of bf16 x [M, K] (K a multiple of 16,
+    rows strided, last dimension contiguous).
+
+    Returns (codes uint8 [M, K/2], two E2M1 codes per byte with element 2i in
+    the low nibble; block_scales float8_e4m3fn [M, K/16]; token_scales fp32
+    [M]); x ~ E2M1 value * block scale * token scale.
+    """
+    import torch
+    _require_cuda(x, codes, block_scales, token_scales)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [M, K] tensor with a contiguous last dimension")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty((M, K // 16), dtype=torch.float8_e4m3fn, device=x.device)
+    if token_scales is None:
+        token_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    for t in (codes, block_scales):
+        if t.dim() != 2 or t.element_size() != 1 or t.stride(1) != 1:
+            raise ValueError("codes / block_scales must be 2-D byte tensors with a contiguous last dimension")
+    if not token_scales.is_contiguous() or token_scales.dtype != torch.float32:
+        raise ValueError("token_scales must be a contiguous fp32 tensor")
+    _check(lib_handle().fmha_quantize_nvfp4(x.data_ptr(), x.stride(0), M, K, codes.data_ptr(), codes.stride(0),
+                                            block_scales.data_ptr(), block_scales.stride(0),
+                                            token_scales.data_ptr(), _stream(stream)))
+    return codes, block_scales, token_scales
 
 
 def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False, block_mask=None,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libfmha.so")
-SOURCES = ["api.cpp", "quantize.hip", "attention.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "nvfp4.hip", "attention.hip"]
 # The attention kernel never sees NaN scores (masked keys are -inf, inputs are
 # finite), so its max reductions need no NaN quieting.  Host validation code
 # keeps full IEEE semantics (it rejects NaN arguments).

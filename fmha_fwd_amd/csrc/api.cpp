@@ -68,7 +68,7 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-uint32_t fmha_abi_version(void) { return 0x000200u; }
+uint32_t fmha_abi_version(void) { return 0x000300u; }
 
 const char* fmha_last_error(void) { return g_last_error.c_str(); }
 
@@ -105,6 +105,37 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes, float* 
   a.nblk = (S + 63) / 64;
   a.out_fmt = codes->dtype == FMHA_DT_INT8 ? fmha::FMT_INT8 : fmha::FMT_E4M3;
   return hip_status(fmha::launch_quantize_blocks(a, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t K, uint8_t* codes,
+                        int64_t codes_row_stride, uint8_t* block_scales, int64_t scales_row_stride,
+                        float* token_scales, fmha_stream_t stream) {
+  if (M < 0) return fail(FMHA_ERR_INVALID, "nvfp4: negative M=%d", M);
+  if (K <= 0 || K % 16 != 0) return fail(FMHA_ERR_INVALID, "nvfp4: K=%d is not a positive multiple of 16", K);
+  if (M == 0) return ok();
+  if (!x || !codes || !block_scales || !token_scales) return fail(FMHA_ERR_INVALID, "nvfp4: null pointer");
+  if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(FMHA_ERR_INVALID, "nvfp4: x not 16-byte aligned");
+  if (x_row_stride < K || x_row_stride % 8 != 0)
+    return fail(FMHA_ERR_INVALID, "nvfp4: x_row_stride=%lld must be >= K and a multiple of 8", (long long)x_row_stride);
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0) return fail(FMHA_ERR_INVALID, "nvfp4: codes not 8-byte aligned");
+  if (codes_row_stride < K / 2 || codes_row_stride % 8 != 0)
+    return fail(FMHA_ERR_INVALID, "nvfp4: codes_row_stride=%lld must be >= K/2 and a multiple of 8",
+                (long long)codes_row_stride);
+  if (scales_row_stride < K / 16)
+    return fail(FMHA_ERR_INVALID, "nvfp4: scales_row_stride=%lld must be >= K/16", (long long)scales_row_stride);
+  if (reinterpret_cast<uintptr_t>(token_scales) % 4 != 0)
+    return fail(FMHA_ERR_INVALID, "nvfp4: token_scales not 4-byte aligned");
+  fmha::Nvfp4Args a{};
+  a.x = static_cast<const uint8_t*>(x);
+  a.x_rs = x_row_stride * 2;
+  a.codes = codes;
+  a.c_rs = codes_row_stride;
+  a.sf = block_scales;
+  a.sf_rs = scales_row_stride;
+  a.ts = token_scales;
+  a.M = M;
+  a.K = K;
+  return hip_status(fmha::launch_quantize_nvfp4(a, static_cast<hipStream_t>(stream)), "nvfp4 launch");
 }
 
 int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {

@@ -21,6 +21,16 @@ struct QuantArgs {
 
 hipError_t launch_quantize_blocks(const QuantArgs& a, hipStream_t stream);
 
+struct Nvfp4Args {
+  const uint8_t* x; int64_t x_rs;   // bf16 [M, K], row stride in bytes
+  uint8_t* codes; int64_t c_rs;     // [M, K/2], two E2M1 codes per byte
+  uint8_t* sf; int64_t sf_rs;       // [M, K/16] E4M3 block scales
+  float* ts;                        // [M] token scales
+  int M, K;                         // K a multiple of 16
+};
+
+hipError_t launch_quantize_nvfp4(const Nvfp4Args& a, hipStream_t stream);
+
 struct FwdArgs {
   const uint8_t* q; int64_t q_sb, q_ss, q_sh;
   const uint8_t* k; int64_t k_sb, k_ss, k_sh;   // paged: sb = page stride, ss = slot stride

@@ -18,6 +18,12 @@ Configurations (d = 128 throughout):
                             blocks active per query block (diagonal always)
   gqa_chunk  the gqa inputs with only the last 256 query positions (a causal
              prefill chunk against 8192 keys)
+
+Per-token NVFP4 quantisation (activation matrices [tokens, hidden], bf16):
+  nvfp4   M=16384 tokens x K=8192 channels (a 16k-token prefill batch of an
+          8192-wide model), spawn key 8; rows N(0, 1) times a per-token
+          magnitude exp(U(-3, 3)), and 0.5% of the channels (41) x20 outliers
+          shared by every token, as in LLM activations
 """
 from dataclasses import dataclass
 
@@ -176,3 +182,29 @@ def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
     return Spec(s.name + f"_S{S}", s.index, B or s.B, Hq or s.Hq, Hkv or s.Hkv, S, s.q_fmt, s.k_fmt, s.v_fmt,
                 kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged),
                 kw.get("page_size", s.page_size), sq=kw.get("sq", 0))
+
+
+NVFP4_SPECS = {"nvfp4": (8, 16384, 8192)}  # name: (spawn key, M tokens, K channels)
+
+
+def nvfp4_activations(M, K, index=8, rows=None):
+    """bf16 activation values [M, K] (float32 array) for the per-token NVFP4
+    quantiser: N(0, 1) rows scaled by exp(U(-3, 3)) per token, 0.5% of the
+    channels x20.  Each group of 256 rows draws from a stream of its own, so
+    `rows` (an index array) returns those rows of the same matrix while
+    drawing only the groups that hold them."""
+    _, _, _, rs, _ = streams(index)
+    mag = np.exp(rs.uniform(-3.0, 3.0, M)).astype(np.float32)
+    n_out = max(1, int(round(0.005 * K)))
+    ch = rs.choice(K, size=n_out, replace=False)
+    idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    x = np.empty((len(idx), K), dtype=np.float32)
+    for grp in np.unique(idx // 256):
+        ss = np.random.SeedSequence(SEED, spawn_key=(index, 1, int(grp)))
+        n = min(256, M - 256 * int(grp))
+        block = np.random.Generator(np.random.PCG64(ss)).standard_normal((n, K), dtype=np.float32)
+        sel = np.nonzero(idx // 256 == grp)[0]
+        x[sel] = block[idx[sel] - 256 * int(grp)]
+    x *= mag[idx][:, None]
+    x[:, ch] *= np.float32(20.0)
+    return to_bf16_values(x)

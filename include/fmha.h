@@ -1,7 +1,7 @@
 /*
  * fmha.h -- C ABI of the MI355X (gfx950) mixed-precision attention forward.
  *
- * Two operations, both enqueued on a caller-supplied HIP stream:
+ * Three operations, each enqueued on a caller-supplied HIP stream:
  *
  *   fmha_quantize_blocks  per-(batch, head, 64-token block) quantisation of a
  *                         bf16 tensor to int8 or E4M3 codes plus one fp32
@@ -12,6 +12,9 @@
  *                         with lazy rescaling, P requantised to the V format,
  *                         causal / GQA / block-sparse / paged-KV options, and
  *                         a bf16 output.
+ *   fmha_quantize_nvfp4   per-token NVFP4 quantisation of a bf16 activation
+ *                         matrix (E2M1 codes, E4M3 16-element block scales,
+ *                         one fp32 scale per token).
  *
  * Sources (FlashInfer pull-request write-ups):
  *   #2711 page "FlashInfer의 DiT 최적화: SageAttention과 Int8/FP8 혼합 정밀도
@@ -26,6 +29,9 @@
  *     최적화": 코드 분석 1 (Q64 x KV256 tiles; query heads per KV head),
  *     코드 분석 2 (block-sparse attention over contiguous or paged K/V taking
  *     q, the paged cache and a page table).
+ *   #3237 page "FlashInfer의 Per-token NVFP4 Quantization 커널 최적화 분석":
+ *     코드 분석 1-2 (per-token NVFP4 quantisation kernel, linear scale-factor
+ *     layout, the input read once for the row maximum and the encoding).
  *
  * Conventions common to every call:
  *   - Every pointer inside a tensor or params struct is a DEVICE pointer;
@@ -180,11 +186,46 @@ typedef struct {
  */
 int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream);
 
+/*
+ * fmha_quantize_nvfp4 -- per-token NVFP4 quantisation (#3237 page, 코드 분석
+ * 1-2).  The page names the kernel but not the format; the public NVFP4
+ * definition is used: E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6),
+ * one E4M3 scale per 16 consecutive elements, one fp32 scale per token.
+ *
+ * For every row r of x [M, K] (fp32 arithmetic, correctly rounded, nearest
+ * even, no flush to zero):
+ *   amax = max |x[r, :]|;
+ *   if amax < 2^-116 (zero rows included): ts = 1, g6 = 0;
+ *   else ts = amax / 2688, g6 = 448 / amax              (2688 = 6 * 448);
+ *   for each block j of 16 elements (bmax = max |x| over the block):
+ *     sf  = E4M3(min(bmax * g6, 448));
+ *     bs  = dec(sf) * ts;
+ *     es  = bs > 0 ? min(1 / bs, FLT_MAX) : 0;
+ *     code[k] = E2M1(x[r, 16j + k] * es)  (saturating at +-6, sign of zero kept);
+ * so x ~ E2M1 value * dec(sf) * ts, and the largest element of a row maps to
+ * +-6 in a block whose scale is 448.
+ *
+ *   x             bf16 [M, K]; row stride x_row_stride in ELEMENTS (>= K, a
+ *                 multiple of 8); 16-byte aligned; read only.
+ *   codes         uint8 [M, K/2]: element 2i in the low nibble of byte i;
+ *                 row stride codes_row_stride in BYTES (>= K/2, a multiple
+ *                 of 8); 8-byte aligned; written.
+ *   block_scales  uint8 [M, K/16] E4M3 bit patterns, linear (row-major);
+ *                 row stride scales_row_stride in BYTES (>= K/16); written.
+ *   token_scales  fp32 [M], contiguous, 4-byte aligned; written.
+ *   K must be a positive multiple of 16; M == 0 is a no-op.  Outputs may not
+ *   overlap x or each other.  Inputs are finite.
+ */
+int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t K,
+                        uint8_t* codes, int64_t codes_row_stride,
+                        uint8_t* block_scales, int64_t scales_row_stride,
+                        float* token_scales, fmha_stream_t stream);
+
 /* Description of the last error on the calling thread ("" after success);
  * valid until the next fmha_* call on that thread. */
 const char* fmha_last_error(void);
 
-/* ABI version: 0xMMmmpp. */
+/* ABI version: 0xMMmmpp (0x000300: fmha_quantize_nvfp4 added). */
 uint32_t fmha_abi_version(void);
 
 #ifdef __cplusplus

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in syms, name
         assert getattr(lib, name) is not None
-    assert lib.fmha_abi_version() == 0x000200
+    assert lib.fmha_abi_version() == 0x000300
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -168,3 +168,34 @@ def test_quantize_rejects_bad_arguments(lib, kw, code, msg):
 def test_quantize_empty_is_a_no_op(lib):
     x, c = _tensor(F.FMHA_DT_BF16), _tensor(F.FMHA_DT_INT8)
     assert lib.fmha_quantize_blocks(ctypes.byref(x), ctypes.byref(c), None, 0, 64, 4, 128, 64, None) == F.FMHA_OK
+
+
+def _nvfp4(lib, **kw):
+    a = dict(x=FAKE, xs=64, M=4, K=64, c=FAKE, cs=32, s=FAKE, ss=4, t=FAKE)
+    a.update(kw)
+    return lib.fmha_quantize_nvfp4(a["x"], a["xs"], a["M"], a["K"], a["c"], a["cs"], a["s"], a["ss"], a["t"], None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(K=40), "multiple of 16"),
+    (dict(K=0), "multiple of 16"),
+    (dict(M=-1), "negative"),
+    (dict(x=0), "null"),
+    (dict(t=0), "null"),
+    (dict(x=FAKE + 8), "x not 16-byte aligned"),
+    (dict(xs=48), "x_row_stride"),
+    (dict(xs=68), "x_row_stride"),
+    (dict(c=FAKE + 4), "codes not 8-byte aligned"),
+    (dict(cs=16), "codes_row_stride"),
+    (dict(cs=36), "codes_row_stride"),
+    (dict(ss=3), "scales_row_stride"),
+    (dict(t=FAKE + 2), "token_scales"),
+])
+def test_nvfp4_rejects_bad_arguments(lib, kw, msg):
+    rc = _nvfp4(lib, **kw)
+    err = lib.fmha_last_error().decode()
+    assert rc == F.FMHA_ERR_INVALID and msg in err, (rc, err)
+
+
+def test_nvfp4_empty_is_a_no_op(lib):
+    assert _nvfp4(lib, M=0, x=0, c=0, s=0, t=0) == F.FMHA_OK
