@@ -5,7 +5,7 @@ current stream; every step of the computation runs in the HIP kernels behind
 the C ABI declared in include/fmha.h.  There is no fallback: if the library is
 missing, importing ``fmha_fwd_amd.lib_handle()`` raises.
 
-    codes, scales = quantize_blocks(x, "e4m3")           # x: bf16 [B,S,H,128]
+    codes, scales = quantize_blocks(x, "e4m3")           # x: bf16 [B,S,H,128 or 192]
     o = fwd(q, k, v, sfs_q=..., sfs_k=..., sfs_v=..., causal=True)
     codes, block_scales, token_scales = quantize_nvfp4(a)  # a: bf16 [M, K]
 """
@@ -121,7 +121,8 @@ def _require_cuda(*ts):
 
 
 def quantize_blocks(x, dtype="e4m3", *, codes=None, scales=None, stream=None):
-    """Per-(batch, head, 64-token block) quantisation of bf16 x [B, S, H, 128].
+    """Per-(batch, head, 64-token block) quantisation of bf16 x [B, S, H, D],
+    D = 128 or 192.
 
     Returns (codes, scales): codes int8 / float8_e4m3fn of x's shape, scales
     fp32 [B, H, ceil(S/64)].
@@ -175,13 +176,15 @@ def quantize_nvfp4(x, *, codes=None, block_scales=None, token_scales=None, strea
 def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False, block_mask=None,
         mask_block=(64, 256), page_table=None, page_size=16, seq_len_kv=None, softmax_scale=None,
         lazy_rescale_log2=8.0, out=None, out_dtype="bf16", sfs_o=None, stream=None):
-    """Attention forward; returns o ([B, Sq, Hq, 128], bf16, or E4M3 when
+    """Attention forward; returns o ([B, Sq, Hq, D], bf16, or E4M3 when
     out_dtype is "e4m3" or `out` is float8_e4m3fn; sfs_o: fp32 [Hq] output
     scale of an E4M3 o, o = encode(O / sfs_o)).
 
-    q: [B, Sq, Hq, 128] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, 128],
-    or with page_table (int32 [B, pages]) pools [num_pages, page_size, Hkv, 128]
-    and seq_len_kv giving Skv.  sfs_*: fp32 [B, H, ceil(S/64)] block scales.
+    q: [B, Sq, Hq, D] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, D],
+    or with page_table (int32 [B, pages]) pools [num_pages, page_size, Hkv, D]
+    and seq_len_kv giving Skv.  D = 128, or 192 for int8 / E4M3 Q and K
+    without block mask or page table.  sfs_*: fp32 [B, H, ceil(S/64)] block
+    scales.
     block_mask: uint8 [B, Hq, ceil(Sq/64), ceil(Skv/256)] (strides honoured;
     last dim contiguous).
     """

@@ -76,7 +76,7 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes, float* 
                          int32_t H, int32_t D, int32_t block_tokens, fmha_stream_t stream) {
   if (!x || !codes) return fail(FMHA_ERR_INVALID, "quantize: null tensor descriptor");
   if (B < 0 || S < 0 || H < 0) return fail(FMHA_ERR_INVALID, "quantize: negative size (B=%d S=%d H=%d)", B, S, H);
-  if (D != 128) return fail(FMHA_ERR_UNSUPPORTED, "quantize: D=%d (only 128 is supported)", D);
+  if (D != 128 && D != 192) return fail(FMHA_ERR_UNSUPPORTED, "quantize: D=%d (128 or 192 are supported)", D);
   if (block_tokens != 64) return fail(FMHA_ERR_UNSUPPORTED, "quantize: block_tokens=%d (only 64 is supported)", block_tokens);
   if (x->dtype != FMHA_DT_BF16) return fail(FMHA_ERR_INVALID, "quantize: x must be bf16");
   if (codes->dtype != FMHA_DT_INT8 && codes->dtype != FMHA_DT_E4M3)
@@ -103,6 +103,7 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes, float* 
   a.S = S;
   a.H = H;
   a.nblk = (S + 63) / 64;
+  a.D = D;
   a.out_fmt = codes->dtype == FMHA_DT_INT8 ? fmha::FMT_INT8 : fmha::FMT_E4M3;
   return hip_status(fmha::launch_quantize_blocks(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
@@ -149,7 +150,7 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   if (p->B < 0 || p->Sq < 0 || p->Skv < 0) return fail(FMHA_ERR_INVALID, "fwd: negative size");
   if (p->Hq < 1 || p->Hkv < 1) return fail(FMHA_ERR_INVALID, "fwd: Hq and Hkv must be >= 1");
   if (p->Hq % p->Hkv != 0) return fail(FMHA_ERR_INVALID, "fwd: Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
-  if (p->D != 128) return fail(FMHA_ERR_UNSUPPORTED, "fwd: D=%d (only 128 is supported)", p->D);
+  if (p->D != 128 && p->D != 192) return fail(FMHA_ERR_UNSUPPORTED, "fwd: D=%d (128 or 192 are supported)", p->D);
   if (p->o.dtype != FMHA_DT_BF16 && p->o.dtype != FMHA_DT_E4M3)
     return fail(FMHA_ERR_UNSUPPORTED, "fwd: o must be bf16 or e4m3");
   if (sfs_o && p->o.dtype != FMHA_DT_E4M3) return fail(FMHA_ERR_INVALID, "fwd: sfs_o given for a bf16 o");
@@ -200,6 +201,7 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
     return fail(FMHA_ERR_UNSUPPORTED, "fwd: K/V token stride of 32 MiB or more");
 
   fmha::FwdKey key{};
+  key.D = p->D;
   key.qf = to_fmt(p->q.dtype);
   key.kf = to_fmt(p->k.dtype);
   key.vf = to_fmt(p->v.dtype);
@@ -212,7 +214,8 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
     return fail(FMHA_ERR_UNSUPPORTED,
                 "fwd: no kernel for (q, k, v) = (%d, %d, %d) with scales (q %d, k %d, v %d); supported: "
                 "bf16/bf16/bf16 unscaled, int8/int8/e4m3 [q,k,v], bf16/bf16/e4m3 [v or none], "
-                "e4m3/e4m3/e4m3 [q,k,v], bf16/e4m3/e4m3 [k,v]",
+                "e4m3/e4m3/e4m3 [q,k,v], bf16/e4m3/e4m3 [k,v]; with D=192 only int8/int8/e4m3 and e4m3/e4m3/e4m3 "
+                "[q,k,v] without a block mask or page table",
                 (int)p->q.dtype, (int)p->k.dtype, (int)p->v.dtype, sb[0], sb[1], sb[2]);
   if (empty) return ok();
 

@@ -96,27 +96,30 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_,
-          bool RP_ = false>
+          bool RP_ = false, int D_ = 128>
 struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
+  static constexpr int D = D_, ND = D / 32;  // head dim; 32-row d-tiles of O^T
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
   // RP: heads packed inside a wave (fewer than 32 rows per head), so a
   // lane's head, Q scale and P scale are its own (two more live registers)
   static constexpr bool RP = RP_;
   static constexpr int MT = QF;                                  // QK operand format
-  static constexpr int WPE = MT == FMT_BF16 || MASKED || PAGED || RP ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
+  static constexpr int WPE =
+      MT == FMT_BF16 || MASKED || PAGED || RP || D != 128 ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
-  static constexpr int KROW = KF == FMT_BF16 ? 256 : 128;        // bytes per K row (HBM and LDS)
-  static constexpr int VROW = VF == FMT_BF16 ? 256 : 128;
+  static constexpr int KROW = KF == FMT_BF16 ? 2 * D : D;        // bytes per K row (HBM and LDS)
+  static constexpr int VROW = VF == FMT_BF16 ? 2 * D : D;
   // LDS rows are padded so that every lane reads at a fixed offset from its
   // own base address without bank conflicts (64 banks x 4 bytes = 16 chunks
-  // of 16 bytes): K rows advance by 17 or 9 chunks, so the 16 consecutive rows
-  // of one MFMA-operand read land in 16 distinct chunks; 128-byte V rows
-  // advance by 10 chunks, so the two 8-row column pairs of a transposing read
-  // (chunks c and c + 1) fall on even and odd chunks respectively.
-  static constexpr int KP = KROW + 16, VP = VROW == 128 ? VROW + 32 : VROW + 16;
+  // of 16 bytes): K rows advance by an odd number of chunks (17, 9 or 13),
+  // so the 16 consecutive rows of one MFMA-operand read land in 16 distinct
+  // chunks; 8-bit V rows advance by an even number of chunks not divisible by
+  // 4 (10 or 14), so the 8 rows of a transposing read land on 8 distinct even
+  // chunks and their neighbours (chunk c + 1) on the odd ones.
+  static constexpr int KP = KROW + 16, VP = VF == FMT_BF16 ? VROW + 16 : VROW + 32;
   static constexpr int K_BUF = kSub * KP, V_BUF = kSub * VP;
   static constexpr int LDS_BYTES = 2 * (K_BUF + V_BUF);
   static constexpr int NT = NW * 64;
@@ -130,10 +133,10 @@ struct Cfg {
 };
 
 // Q operand registers of one lane (query l % 32, contraction slice of group g).
-template <int MT> struct QRegs;
-template <> struct QRegs<FMT_BF16> { v8bf r[8]; };  // d = 64g + 8t .. +8, t = 0..7
-template <> struct QRegs<FMT_E4M3> { v8i r[2]; };   // bytes 64t + 32g .. +32
-template <> struct QRegs<FMT_INT8> { v4i r[4]; };   // bytes 32t + 16g .. +16
+template <int MT, int D> struct QRegs;
+template <int D> struct QRegs<FMT_BF16, D> { v8bf r[D / 16]; };  // d = (D/2)g + 8t .. +8
+template <int D> struct QRegs<FMT_E4M3, D> { v8i r[D / 64]; };   // bytes 64t + 32g .. +32
+template <int D> struct QRegs<FMT_INT8, D> { v4i r[D / 32]; };   // bytes 32t + 16g .. +16
 
 template <int MT> struct SAcc { v16f r[2]; };
 template <> struct SAcc<FMT_INT8> { v16i r[2]; };
@@ -465,26 +468,26 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
   };
   // ---- Q tile into registers (B operand of S^T = K Q^T)
-  QRegs<C::MT> q;
+  QRegs<C::MT, C::D> q;
   {
     const bool ok = qi < a.Sq;
     const uint8_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)(ok ? qi : 0) * a.q_ss;
     if constexpr (C::MT == FMT_BF16) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        uint4 u = ok ? *(const uint4*)(qp + 128 * g + 16 * t) : make_uint4(0, 0, 0, 0);
+      for (int t = 0; t < C::D / 16; ++t) {
+        uint4 u = ok ? *(const uint4*)(qp + C::D * g + 16 * t) : make_uint4(0, 0, 0, 0);
         q.r[t] = __builtin_bit_cast(v8bf, u);
       }
     } else if constexpr (C::MT == FMT_E4M3) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < C::D / 64; ++t) {
         uint4 u0 = ok ? *(const uint4*)(qp + 64 * t + 32 * g) : make_uint4(0, 0, 0, 0);
         uint4 u1 = ok ? *(const uint4*)(qp + 64 * t + 32 * g + 16) : make_uint4(0, 0, 0, 0);
         q.r[t] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < C::D / 32; ++t) {
         uint4 u = ok ? *(const uint4*)(qp + 32 * t + 16 * g) : make_uint4(0, 0, 0, 0);
         q.r[t] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
       }
@@ -520,8 +523,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // ---- per-lane LDS read bases (stage-relative; every operand read is a
   //      fixed immediate offset from these)
   int kb_lane;
-  if constexpr (C::WIDEN) kb_lane = m32 * C::KP + 64 * g;
-  else if constexpr (C::MT == FMT_BF16) kb_lane = m32 * C::KP + 128 * g;
+  if constexpr (C::WIDEN) kb_lane = m32 * C::KP + (C::D / 2) * g;
+  else if constexpr (C::MT == FMT_BF16) kb_lane = m32 * C::KP + C::D * g;
   else if constexpr (C::MT == FMT_E4M3) kb_lane = m32 * C::KP + 32 * g;
   else kb_lane = m32 * C::KP + 16 * g;
   const int tr_G = lane >> 4;
@@ -540,18 +543,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     const lds_u8* kp = kb + kb_lane;
     if constexpr (C::WIDEN) {
       // E4M3 K: one 16-byte read holds the operands of two MFMAs (d =
-      // 64g + 16j .. +16), widened to bf16 just before use
-      uint4 kr[2][4];
+      // (D/2)g + 16j .. +16), widened to bf16 just before use
+      uint4 kr[2][C::D / 32];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kr[T][j] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * j);
+        for (int j = 0; j < C::D / 32; ++j) kr[T][j] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * j);
       if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < C::D / 32; ++j) {
           acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].x, kr[T][j].y), q.r[2 * j], acc.r[T]);
           acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].z, kr[T][j].w), q.r[2 * j + 1], acc.r[T]);
         }
@@ -561,56 +564,57 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       // operands (one 32-key tile) in flight at a time
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        uint4 kr[8];
+        uint4 kr[C::D / 16];
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) kr[tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
+        for (int tt = 0; tt < C::D / 16; ++tt) kr[tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
         if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
         acc.r[T] = v16f{};
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[tt], acc.r[T]);
+        for (int tt = 0; tt < C::D / 16; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[tt], acc.r[T]);
       }
     } else if constexpr (C::MT == FMT_BF16) {
-      uint4 kr[2][8];
+      uint4 kr[2][C::D / 16];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
+        for (int tt = 0; tt < C::D / 16; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
       if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[T][tt]), q.r[tt], acc.r[T]);
+        for (int tt = 0; tt < C::D / 16; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[T][tt]), q.r[tt], acc.r[T]);
       }
     } else if constexpr (C::MT == FMT_E4M3) {
-      uint4 kr[2][4];
+      uint4 kr[2][C::D / 32];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kr[T][i] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 64 * (i >> 1) + 16 * (i & 1));
+        for (int i = 0; i < C::D / 32; ++i)
+          kr[T][i] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 64 * (i >> 1) + 16 * (i & 1));
       if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16f{};
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < C::D / 64; ++tt) {
           const uint4 u0 = kr[T][2 * tt], u1 = kr[T][2 * tt + 1];
           const v8i av = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           acc.r[T] = mfma_f8(av, q.r[tt], acc.r[T]);
         }
       }
     } else {
-      uint4 kr[2][4];
+      uint4 kr[2][C::D / 32];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 32 * tt);
+        for (int tt = 0; tt < C::D / 32; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 32 * tt);
       if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         acc.r[T] = v16i{};
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < C::D / 32; ++tt) {
           const uint4 u = kr[T][tt];
           acc.r[T] = mfma_i8(v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}, q.r[tt], acc.r[T]);
         }
@@ -630,14 +634,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     return acc;
   };
 
-  // ---- per-lane state.  O^T (4 tiles of 32 d x 32 queries) is kept in units
+  // ---- per-lane state.  O^T (D/32 tiles of 32 d x 32 queries) is kept in units
   // of the reference V scale `sv_ref`: before a sub-tile's PV product is
   // accumulated, O is multiplied by alpha_row * sv_ref / sv_tile (one multiply
   // folds the lazy rescale and the change of V block scale), then the MFMA
   // accumulates codes x codes directly.
-  v16f o[4];
+  v16f o[C::ND];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) o[d] = v16f{};
+  for (int d = 0; d < C::ND; ++d) o[d] = v16f{};
   float m_run = -kInf;
   // Row sums of P.  With E4M3 P they come from the matrix core: a 16x16x128
   // product of a 0/1 matrix with the P operand (read as 128 x 16) whose row
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 
   // Softmax of one sub-tile, written as eight stages of separable work:
   //   0: row max, lazy decision, rescale of den (and of O off the fast path);
-  //   1-2: rescale of O, two d-tiles each (fast V-reference path);
+  //   1-2: rescale of O, half the d-tiles each (fast V-reference path);
   //   3-6: P = 2^(s2 - m) / sp for eight keys each, clamped to the E4M3 range
   //        only where P / sp can reach it (sfs_p given or tau above log2 448);
   //   7: P to the PV operand format (bf16 P: also den += P).
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       } else {
         if (__ballot(trig) != 0) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d)
+          for (int d = 0; d < C::ND; ++d)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
         }
@@ -746,7 +750,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     } else if constexpr (K == 1 || K == 2) {
       if constexpr (C::VS && DIRECT) {
 #pragma unroll
-        for (int d = 2 * (K - 1); d < 2 * K; ++d)
+        for (int d = (C::ND / 2) * (K - 1); d < (K == 2 ? C::ND : C::ND / 2); ++d)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[d][r] *= st.fo;
       }
@@ -809,7 +813,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     constexpr bool DIRECT = decltype(direct_tag)::value;
     den_acc = mfma_f8_16(ones_a, pt.pb, den_acc);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < C::ND; ++d) {
       if constexpr (!C::VS || DIRECT) {
         o[d] = mfma_f8(vop[d], pt.pb, o[d]);
       } else {
@@ -822,14 +826,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   auto pv = [&](const PTile& pt, const lds_u8* vb, auto direct_tag) {
     const lds_u8* vp = vb + vb_lane;
     if constexpr (C::VF == FMT_E4M3) {
-      v8i vop[4];
+      v8i vop[C::ND];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vb, d);
+      for (int d = 0; d < C::ND; ++d) vop[d] = read_vop(vb, d);
       pv_e4m3(pt, vop, direct_tag);
     } else {
       // bf16 P and V (V unscaled).
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < C::ND; ++d) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           uint32_t w[4];
@@ -869,7 +873,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // issuing the S MFMAs (32 more live registers) and issue the copies of the
   // next sub-tile after that, in the shadow of those MFMAs; the others issue
   // the copies first and read V in the PV step.
-  constexpr bool EARLY_V = C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED;
+  constexpr bool EARLY_V = C::VF == FMT_E4M3 && C::WPE == 2 && !C::MASKED && !C::PAGED && C::D == 128;
   // The buffer holding sub-tile tc: the captured `buf`, toggled by each
   // step, or (unrolled dense loop) a compile-time 0 / 1, so that LDS
   // addresses fold into the instructions.
@@ -889,9 +893,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     int tnn = n_sub;
     if constexpr (EARLY_V) {
       const SAcc<C::MT> acc = qk_raised(kbuf0 + bv * C::K_BUF);
-      v8i vop[4];
+      v8i vop[C::ND];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) vop[d] = read_vop(vbuf0 + bv * C::V_BUF, d);
+      for (int d = 0; d < C::ND; ++d) vop[d] = read_vop(vbuf0 + bv * C::V_BUF, d);
       issue_next(tnn, bv);
       __builtin_amdgcn_sched_barrier(0);
       pv_e4m3(softmax_p(acc, tc, edge_tag, clamp_tag, direct_tag), vop, direct_tag);
@@ -951,7 +955,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     // E4M3 output: encode(O / sfs_o), nearest-even, saturating at +-448
     const float f = a.sfs_o ? inv / a.sfs_o[hq] : inv;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < C::ND; ++d) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         float x[4];
@@ -965,7 +969,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     return;
   }
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < C::ND; ++d) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int dd = 32 * d + 8 * a4 + 4 * g;
@@ -1019,6 +1023,15 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
 }  // namespace
 
 bool fwd_supported(const FwdKey& k) {
+  if (k.D == 192) {
+    // head dim 192: dense or causal, 8-bit Q and K (the Q operand, O and the
+    // K reads fit two wavefronts per SIMD only with 8-bit QK)
+    if (k.masked || k.paged) return false;
+    if (k.qf == FMT_INT8 && k.kf == FMT_INT8 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
+    if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
+    return false;
+  }
+  if (k.D != 128) return false;
   if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_BF16)
     return !k.q_scaled && !k.k_scaled && !k.v_scaled;
   if (k.qf == FMT_INT8 && k.kf == FMT_INT8 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
@@ -1055,6 +1068,13 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
 
 hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
   if (!fwd_supported(k)) return hipErrorInvalidValue;
+  if (k.D == 192) {
+    // no heads packed inside a wave (that needs the RP instances); whole-wave
+    // head packing is a run-time choice of the same instance
+    if (k.qf == FMT_INT8)
+      return launch<Cfg<FMT_INT8, FMT_INT8, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);
+    return launch<Cfg<FMT_E4M3, FMT_E4M3, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);
+  }
   if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_BF16)
     return dispatch_layout<FMT_BF16, FMT_BF16, FMT_BF16, false, false, false>(k, a, s);
   if (k.qf == FMT_INT8)

@@ -16,6 +16,7 @@ struct QuantArgs {
   int64_t c_sb, c_ss, c_sh;
   float* scales;
   int B, S, H, nblk;
+  int D;        // 128 or 192
   int out_fmt;  // FMT_INT8 or FMT_E4M3
 };
 
@@ -61,6 +62,7 @@ struct FwdArgs {
 };
 
 struct FwdKey {
+  int D;                // head dim: 128, or 192 for some keys
   int qf, kf, vf;
   bool q_scaled, k_scaled, v_scaled;
   bool masked, paged;

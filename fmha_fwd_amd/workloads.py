@@ -6,7 +6,7 @@ PCG64 with ``SeedSequence(2711, spawn_key=(config index,))`` spawned into five
 child streams used in the order [Q, K, V, structure, mask]; normal draws are
 float32 rounded to bf16 (torch's round-to-nearest-even cast).
 
-Configurations (d = 128 throughout):
+Configurations (d = 128 throughout; `small_spec` can set d = 192):
   tiny    B=1 H=2  S=256    all bf16, unscaled, non-causal
   dit_i8  B=1 H=24 S=4096   int8 Q/K + E4M3 V with 64-token block scales,
                             2% outlier channels (3 per head) of Q and K x20
@@ -18,6 +18,8 @@ Configurations (d = 128 throughout):
                             blocks active per query block (diagonal always)
   gqa_chunk  the gqa inputs with only the last 256 query positions (a causal
              prefill chunk against 8192 keys)
+  dit_i8_d192, gqa_d192  the dit_i8 and gqa shapes and formats at head dim
+             192 (own spawn keys 9 and 10)
 
 Per-token NVFP4 quantisation (activation matrices [tokens, hidden], bf16):
   nvfp4   M=16384 tokens x K=8192 channels (a 16k-token prefill batch of an
@@ -92,6 +94,9 @@ SPECS = {
     "gqa_step": Spec("gqa_step", 6, 64, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=16),
     # the same step with four query heads per KV head (32 / 8)
     "gqa4_step": Spec("gqa4_step", 7, 64, 32, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, sq=16),
+    # head dim 192 (index 8 is the NVFP4 activations' spawn key)
+    "dit_i8_d192": Spec("dit_i8_d192", 9, 1, 24, 24, 4096, "int8", "int8", "e4m3", D=192),
+    "gqa_d192": Spec("gqa_d192", 10, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, D=192),
 }
 
 
@@ -181,7 +186,7 @@ def small_spec(base, S, B=None, Hq=None, Hkv=None, **kw):
     s = SPECS[base]
     return Spec(s.name + f"_S{S}", s.index, B or s.B, Hq or s.Hq, Hkv or s.Hkv, S, s.q_fmt, s.k_fmt, s.v_fmt,
                 kw.get("causal", s.causal), kw.get("masked", s.masked), kw.get("paged", s.paged),
-                kw.get("page_size", s.page_size), sq=kw.get("sq", 0))
+                kw.get("page_size", s.page_size), D=kw.get("D", s.D), sq=kw.get("sq", 0))
 
 
 NVFP4_SPECS = {"nvfp4": (8, 16384, 8192)}  # name: (spawn key, M tokens, K channels)

@@ -24,7 +24,8 @@
  *   #5900 page "Blackwell 아키텍처를 위한 FlashInfer의 FP8/BF16 혼합 정밀도
  *     Attention 최적화 분석": title and 코드 분석 1 (QK in bf16 or fp8, PV in
  *     fp8, 16-bit output, head dim 128), 코드 분석 3 (lazy correction: O is
- *     rescaled only when the row maximum grows by 2^8).
+ *     rescaled only when the row maximum grows by 2^8), 리뷰어 피드백 반영
+ *     (head dim 192 and an FP8 output as configurations of the family).
  *   #4474 page "FlashInfer의 PrimTS를 활용한 고성능 Block-Sparse Attention
  *     최적화": 코드 분석 1 (Q64 x KV256 tiles; query heads per KV head),
  *     코드 분석 2 (block-sparse attention over contiguous or paged K/V taking
@@ -101,7 +102,8 @@ typedef void* fmha_stream_t;
  *   codes   [B, S, H, D] int8 or E4M3 (codes->dtype); written.  May not
  *           overlap x.
  *   scales  fp32 [B, H, ceil(S / block_tokens)], contiguous; written.
- *   D must be 128 and block_tokens 64.  B, S or H equal to 0 is a no-op.
+ *   D must be 128 or 192 and block_tokens 64.  B, S or H equal to 0 is a
+ *   no-op.
  */
 int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes,
                          float* scales, int32_t B, int32_t S, int32_t H,
@@ -113,8 +115,10 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes,
  */
 typedef struct {
   uint32_t struct_size;
-  int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128; Hq % Hkv == 0; query head h
-                                      reads key/value head h / (Hq / Hkv) */
+  int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128, or 192 for the 8-bit-QK keys
+                                      without block mask or page table;
+                                      Hq % Hkv == 0; query head h reads
+                                      key/value head h / (Hq / Hkv) */
   /* q: [B, Sq, Hq, D]; o: [B, Sq, Hq, D] bf16 or E4M3 (written).
    * k, v contiguous-cache case: [B, Skv, Hkv, D].
    * k, v paged case (page_table != NULL): pools [num_pages, page_size, Hkv, D]

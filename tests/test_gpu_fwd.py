@@ -320,6 +320,18 @@ def test_small_causal_gqa_packed(S):
     _run_small(W.small_spec("gqa", S, B=2, Hq=8, Hkv=2, causal=True))
 
 
+@pytest.mark.parametrize("base,B,Hq,Hkv,causal,sq", [("dit_i8", 1, 3, 3, False, 0), ("gqa", 2, 8, 2, True, 0),
+                                                      ("gqa", 1, 4, 2, False, 0), ("gqa", 2, 8, 2, True, 100),
+                                                      ("dit_i8", 2, 2, 1, True, 0)])
+@pytest.mark.parametrize("S", [1, 65, 320, 1000])
+def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
+    # head dim 192 with 8-bit Q and K: dense, causal, GQA (whole-wave head
+    # packing for the causal groups), a query chunk, ragged tails
+    if sq >= S:
+        sq = 0
+    _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv, causal=causal, sq=sq, D=192))
+
+
 def test_deterministic():
     spec = W.small_spec("gqa", 700, B=1, Hq=8, Hkv=2, causal=True)
     data = W.generate(spec)
@@ -337,6 +349,8 @@ FULL = [
     ("gqa", [(0, 0), (0, 7), (1, 63)], "sample"),
     ("sparse", [(0, 0), (3, 31)], "sample"),
     ("gqa_chunk", [(0, 0), (1, 63)], None),
+    ("dit_i8_d192", [(0, 0), (0, 23)], "sample"),
+    ("gqa_d192", [(0, 0), (1, 63)], "sample"),
 ]
 
 

@@ -92,3 +92,16 @@ def test_full_workloads_bit_exact(name, which, heads, workload_cache):
     if heads is not None:
         x, c, s = x[:, :, heads], c[:, :, heads], s[:, heads]
     _check(x, fmt, c, s)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+@pytest.mark.parametrize("shape", [(1, 130, 3, 192), (2, 64, 2, 192), (1, 1, 1, 192), (3, 257, 5, 192)])
+def test_head_dim_192_bit_exact(fmt, shape):
+    print(f"quantize {fmt} {shape}", flush=True)
+    rng = np.random.default_rng(hash(shape) % 2 ** 32)
+    x = rng.standard_normal(shape).astype(np.float32)
+    x *= np.exp(rng.uniform(-6, 6, (shape[0], 1, shape[2], 1))).astype(np.float32)
+    x[0, :min(64, shape[1]), 0] = 0.0          # a zero block
+    x = _bf16(x)
+    _, c, s = _gpu_quant(x, fmt)
+    _check(x, fmt, c, s)
