@@ -559,6 +559,23 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
           acc.r[T] = mfma_bf16(e4m3x8_to_bf16(kr[T][j].z, kr[T][j].w), q.r[2 * j + 1], acc.r[T]);
         }
       }
+    } else if constexpr (C::MT == FMT_BF16 && C::D != 128) {
+      // bf16 at head dim 192: a quarter of the K operands in flight at a time
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint4 kr[C::D / 32];
+#pragma unroll
+          for (int tt = 0; tt < C::D / 32; ++tt)
+            kr[tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * ((C::D / 32) * h + tt));
+          if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
+          if (h == 0) acc.r[T] = v16f{};
+#pragma unroll
+          for (int tt = 0; tt < C::D / 32; ++tt)
+            acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[(C::D / 32) * h + tt], acc.r[T]);
+        }
+      }
     } else if constexpr (C::MT == FMT_BF16 && (C::MASKED || C::PAGED)) {
       // masked / paged instances keep more copy state live: half the K
       // operands (one 32-key tile) in flight at a time
@@ -914,9 +931,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   auto run = [&](auto clamp_tag, auto direct_tag) {
     // sub-tiles valid for every pair of the workgroup first (a block mask
     // only skips whole sub-tiles), then the edge ones; dense contiguous
-    // instances take the first kind two per trip with the buffers fixed (the
-    // others have no registers to spare for the longer loop)
-    if constexpr (!C::MASKED && !C::PAGED) {
+    // instances at head dim 128 take the first kind two per trip with the
+    // buffers fixed (the others have no registers to spare for the longer
+    // loop)
+    if constexpr (!C::MASKED && !C::PAGED && C::D == 128) {
       while (tc < n_sub && tc < full_end) {
         [[clang::always_inline]] step(std::false_type{}, clamp_tag, direct_tag, std::integral_constant<int, 0>{});
         if (!(tc < n_sub && tc < full_end)) {
@@ -1024,11 +1042,14 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
 
 bool fwd_supported(const FwdKey& k) {
   if (k.D == 192) {
-    // head dim 192: dense or causal, 8-bit Q and K (the Q operand, O and the
-    // K reads fit two wavefronts per SIMD only with 8-bit QK)
+    // head dim 192: dense or causal, 8-bit Q and K, or bf16 Q and K with a
+    // scaled E4M3 V (the DiT formats); bf16 Q and K read a quarter of the K
+    // operands at a time so that Q, O and the reads fit two wavefronts per
+    // SIMD
     if (k.masked || k.paged) return false;
     if (k.qf == FMT_INT8 && k.kf == FMT_INT8 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
     if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
+    if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_E4M3) return !k.q_scaled && !k.k_scaled && k.v_scaled;
     return false;
   }
   if (k.D != 128) return false;
@@ -1071,6 +1092,8 @@ hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
   if (k.D == 192) {
     // no heads packed inside a wave (that needs the RP instances); whole-wave
     // head packing is a run-time choice of the same instance
+    if (k.qf == FMT_BF16)
+      return launch<Cfg<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, true, false, false, kDenseWaves, false, 192>>(a, s);
     if (k.qf == FMT_INT8)
       return launch<Cfg<FMT_INT8, FMT_INT8, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);
     return launch<Cfg<FMT_E4M3, FMT_E4M3, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);

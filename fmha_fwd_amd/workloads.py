@@ -18,8 +18,8 @@ Configurations (d = 128 throughout; `small_spec` can set d = 192):
                             blocks active per query block (diagonal always)
   gqa_chunk  the gqa inputs with only the last 256 query positions (a causal
              prefill chunk against 8192 keys)
-  dit_i8_d192, gqa_d192  the dit_i8 and gqa shapes and formats at head dim
-             192 (own spawn keys 9 and 10)
+  dit_i8_d192, gqa_d192, dit_d192  the dit_i8, gqa and dit shapes and
+             formats at head dim 192 (own spawn keys 9, 10 and 11)
 
 Per-token NVFP4 quantisation (activation matrices [tokens, hidden], bf16):
   nvfp4   M=16384 tokens x K=8192 channels (a 16k-token prefill batch of an
@@ -97,6 +97,7 @@ SPECS = {
     # head dim 192 (index 8 is the NVFP4 activations' spawn key)
     "dit_i8_d192": Spec("dit_i8_d192", 9, 1, 24, 24, 4096, "int8", "int8", "e4m3", D=192),
     "gqa_d192": Spec("gqa_d192", 10, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, D=192),
+    "dit_d192": Spec("dit_d192", 11, 1, 40, 40, 32760, "bf16", "bf16", "e4m3", D=192),
 }
 
 

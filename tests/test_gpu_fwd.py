@@ -322,11 +322,13 @@ def test_small_causal_gqa_packed(S):
 
 @pytest.mark.parametrize("base,B,Hq,Hkv,causal,sq", [("dit_i8", 1, 3, 3, False, 0), ("gqa", 2, 8, 2, True, 0),
                                                       ("gqa", 1, 4, 2, False, 0), ("gqa", 2, 8, 2, True, 100),
-                                                      ("dit_i8", 2, 2, 1, True, 0)])
+                                                      ("dit_i8", 2, 2, 1, True, 0), ("dit", 1, 2, 2, False, 0),
+                                                      ("dit", 2, 4, 2, True, 0)])
 @pytest.mark.parametrize("S", [1, 65, 320, 1000])
 def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
-    # head dim 192 with 8-bit Q and K: dense, causal, GQA (whole-wave head
-    # packing for the causal groups), a query chunk, ragged tails
+    # head dim 192 with 8-bit Q and K, or bf16 Q and K with E4M3 V: dense,
+    # causal, GQA (whole-wave head packing for the causal groups), a query
+    # chunk, ragged tails
     if sq >= S:
         sq = 0
     _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv, causal=causal, sq=sq, D=192))
@@ -351,6 +353,7 @@ FULL = [
     ("gqa_chunk", [(0, 0), (1, 63)], None),
     ("dit_i8_d192", [(0, 0), (0, 23)], "sample"),
     ("gqa_d192", [(0, 0), (1, 63)], "sample"),
+    ("dit_d192", [(0, 0), (0, 39)], "sample"),
 ]
 
 
