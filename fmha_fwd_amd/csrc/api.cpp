@@ -113,6 +113,7 @@ int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t 
                         float* token_scales, fmha_stream_t stream) {
   if (M < 0) return fail(FMHA_ERR_INVALID, "nvfp4: negative M=%d", M);
   if (K <= 0 || K % 16 != 0) return fail(FMHA_ERR_INVALID, "nvfp4: K=%d is not a positive multiple of 16", K);
+  if (K > (1 << 28)) return fail(FMHA_ERR_UNSUPPORTED, "nvfp4: K=%d above 2^28 (32-bit in-row offsets)", K);
   if (M == 0) return ok();
   if (!x || !codes || !block_scales || !token_scales) return fail(FMHA_ERR_INVALID, "nvfp4: null pointer");
   if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(FMHA_ERR_INVALID, "nvfp4: x not 16-byte aligned");

@@ -218,7 +218,8 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream);
  *   block_scales  uint8 [M, K/16] E4M3 bit patterns, linear (row-major);
  *                 row stride scales_row_stride in BYTES (>= K/16); written.
  *   token_scales  fp32 [M], contiguous, 4-byte aligned; written.
- *   K must be a positive multiple of 16; M == 0 is a no-op.  Outputs may not
+ *   K must be a positive multiple of 16 (at most 2^28, else
+ *   FMHA_ERR_UNSUPPORTED); M == 0 is a no-op.  Outputs may not
  *   overlap x or each other.  Inputs are finite.
  */
 int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t K,

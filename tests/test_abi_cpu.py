@@ -201,5 +201,10 @@ def test_nvfp4_rejects_bad_arguments(lib, kw, msg):
     assert rc == F.FMHA_ERR_INVALID and msg in err, (rc, err)
 
 
+def test_nvfp4_rejects_rows_beyond_2_28(lib):
+    rc = _nvfp4(lib, K=(1 << 28) + 16, xs=(1 << 28) + 16, cs=(1 << 27) + 8, ss=(1 << 24) + 1)
+    assert rc == F.FMHA_ERR_UNSUPPORTED and "2^28" in lib.fmha_last_error().decode()
+
+
 def test_nvfp4_empty_is_a_no_op(lib):
     assert _nvfp4(lib, M=0, x=0, c=0, s=0, t=0) == F.FMHA_OK

@@ -146,9 +146,11 @@ def test_kv_sequence_beyond_2gib():
     del kbig, vbig
 
 
-@pytest.mark.parametrize("base,S,causal", [("tiny", 200, False), ("dit", 320, False), ("dit_i8", 300, False),
-                                           ("gqa", 300, True), ("sparse", 300, False)])
-def test_e4m3_output(base, S, causal):
+@pytest.mark.parametrize("base,S,causal,D", [("tiny", 200, False, 128), ("dit", 320, False, 128),
+                                             ("dit_i8", 300, False, 128), ("gqa", 300, True, 128),
+                                             ("sparse", 300, False, 128), ("dit", 320, False, 192),
+                                             ("gqa", 300, True, 192)])
+def test_e4m3_output(base, S, causal, D):
     # O / sfs_o encoded to E4M3 in the epilogue; the per-head scales spread
     # the outputs over the E4M3 range (saturation and subnormals included).
     # Bar: each code is the encoding of a value within tol of the oracle's
@@ -159,7 +161,7 @@ def test_e4m3_output(base, S, causal):
     # from the oracle's own encoding.
     from oracle.attention import output_e4m3
     from oracle.codecs import e4m3_decode
-    spec = W.small_spec(base, S, B=1, Hq=4, Hkv=2, causal=causal)
+    spec = W.small_spec(base, S, B=1, Hq=4, Hkv=2, causal=causal, D=D)
     print(f"fwd e4m3 output {spec}", flush=True)
     data = W.generate(spec)
     so = np.array([2.0 ** -11, 0.004, 0.02, 1.0], dtype=np.float32)
