@@ -325,7 +325,8 @@ def test_small_causal_gqa_packed(S):
 @pytest.mark.parametrize("base,B,Hq,Hkv,causal,sq", [("dit_i8", 1, 3, 3, False, 0), ("gqa", 2, 8, 2, True, 0),
                                                       ("gqa", 1, 4, 2, False, 0), ("gqa", 2, 8, 2, True, 100),
                                                       ("dit_i8", 2, 2, 1, True, 0), ("dit", 1, 2, 2, False, 0),
-                                                      ("dit", 2, 4, 2, True, 0)])
+                                                      ("dit", 2, 4, 2, True, 0), ("gqa", 2, 16, 2, True, 5),
+                                                      ("dit", 1, 16, 2, False, 3)])
 @pytest.mark.parametrize("S", [1, 65, 320, 1000])
 def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
     # head dim 192 with 8-bit Q and K, or bf16 Q and K with E4M3 V: dense,
