@@ -35,9 +35,9 @@
  *     layout, the input read once for the row maximum and the encoding).
  *
  * Conventions common to every call:
- *   - Every pointer inside a tensor or params struct is a DEVICE pointer;
- *     the structs themselves live in host memory and are read during the call
- *     only.  The caller owns every buffer; the library allocates nothing and
+ *   - Every data pointer (an argument, or inside a tensor or params struct)
+ *     is a DEVICE pointer; the structs themselves live in host memory and are
+ *     read during the call only.  The caller owns every buffer; the library allocates nothing and
  *     keeps no pointer after returning.
  *   - Arguments are validated before any HIP call.  On a validation failure
  *     nothing is enqueued and the call returns FMHA_ERR_INVALID or
@@ -46,7 +46,9 @@
  *     synchronisation.  A launch error returns FMHA_ERR_HIP.
  *   - Results are deterministic: identical inputs give identical bits.
  *   - Calls on different streams may overlap; the library has no global
- *     mutable state other than the thread-local error string.
+ *     mutable state other than the thread-local error string and a per-kernel
+ *     flag recording that its LDS-size attribute was set (setting it twice
+ *     is harmless).
  */
 #ifndef FMHA_H_
 #define FMHA_H_
