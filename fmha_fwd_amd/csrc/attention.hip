@@ -534,9 +534,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   else  // bf16 V: source row 16g + r, byte column 32(G%2) + 8h'
     vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 2)) * C::VP + 32 * (tr_G & 1) + 8 * (lane & 3);
 
-  // S^T for one sub-tile from the K buffer `kb`.  All K operand reads are
-  // issued before the first MFMA, so each MFMA waits only for its own operand
-  // and the LDS latency hides behind the MFMAs ahead of it.
+  // S^T for one sub-tile from the K buffer `kb`.  The K operand reads of a
+  // group (all of them for 8-bit K; a 32-key tile, or a quarter of one at
+  // head dim 192, for bf16) are issued before its first MFMA, so each MFMA
+  // waits only for its own operand and the LDS latency hides behind the
+  // MFMAs ahead of it.
   auto qk = [&](const lds_u8* kb, auto fence_tag) {
     constexpr bool FENCE = decltype(fence_tag)::value;
     SAcc<C::MT> acc;
@@ -576,9 +578,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
             acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[(C::D / 32) * h + tt], acc.r[T]);
         }
       }
-    } else if constexpr (C::MT == FMT_BF16 && (C::MASKED || C::PAGED)) {
-      // masked / paged instances keep more copy state live: half the K
-      // operands (one 32-key tile) in flight at a time
+    } else if constexpr (C::MT == FMT_BF16) {
+      // half the K operands (one 32-key tile) in flight at a time: the
+      // fewer live registers schedule slightly better than all of them
+      // (measured +0.3-0.8 % on the dense bf16 loop), and masked / paged
+      // instances need the room for their copy state
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         uint4 kr[C::D / 16];
@@ -588,19 +592,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         acc.r[T] = v16f{};
 #pragma unroll
         for (int tt = 0; tt < C::D / 16; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[tt]), q.r[tt], acc.r[T]);
-      }
-    } else if constexpr (C::MT == FMT_BF16) {
-      uint4 kr[2][C::D / 16];
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int tt = 0; tt < C::D / 16; ++tt) kr[T][tt] = *FMHA_LDS(const uint4, kp + 32 * T * C::KP + 16 * tt);
-      if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        acc.r[T] = v16f{};
-#pragma unroll
-        for (int tt = 0; tt < C::D / 16; ++tt) acc.r[T] = mfma_bf16(__builtin_bit_cast(v8bf, kr[T][tt]), q.r[tt], acc.r[T]);
       }
     } else if constexpr (C::MT == FMT_E4M3) {
       uint4 kr[2][C::D / 32];
