@@ -173,6 +173,39 @@ def quantize_nvfp4(x, *, codes=None, block_scales=None, token_scales=None, strea
     return codes, block_scales, token_scales
 
 
+def _check_shapes(q, k, v, out, sfs_q, sfs_k, sfs_v, sfs_p, sfs_o, block_mask, mask_block, page_table, page_size,
+                  Skv, Hkv):
+    """The C ABI sees pointers and strides only: every extent the kernels
+    index with is checked here against q's [B, Sq, Hq, D]."""
+    B, Sq, Hq, D = q.shape
+
+    def need(cond, what):
+        if not cond:
+            raise ValueError(what)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        need(t.dim() == 4, f"{name} must be 4-D")
+    if page_table is None:
+        need(tuple(k.shape) == (B, Skv, Hkv, D), f"k must be [B, Skv, Hkv, D] = [{B}, {Skv}, {Hkv}, {D}], got {tuple(k.shape)}")
+    else:
+        need(k.shape[1] == page_size and k.shape[3] == D,
+             f"paged k must be [pages, {page_size}, Hkv, {D}], got {tuple(k.shape)}")
+        need(page_table.dim() == 2 and page_table.shape[0] == B and page_table.shape[1] * page_size >= Skv,
+             f"page_table must be [B, >= ceil(Skv / page_size)] = [{B}, {-(-Skv // page_size)}]")
+    need(tuple(v.shape) == tuple(k.shape), f"v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
+    need(tuple(out.shape) == (B, Sq, Hq, D), f"out must be [B, Sq, Hq, D] = [{B}, {Sq}, {Hq}, {D}]")
+    for name, t, H, S in (("sfs_q", sfs_q, Hq, Sq), ("sfs_k", sfs_k, Hkv, Skv), ("sfs_v", sfs_v, Hkv, Skv)):
+        if t is not None:
+            need(tuple(t.shape) == (B, H, -(-S // 64)), f"{name} must be [B, H, ceil(S / 64)] = [{B}, {H}, {-(-S // 64)}]")
+    for name, t in (("sfs_p", sfs_p), ("sfs_o", sfs_o)):
+        if t is not None:
+            need(t.numel() >= Hq, f"{name} needs Hq = {Hq} entries")
+    if block_mask is not None:
+        bq, bkv = mask_block
+        want = (B, Hq, -(-Sq // bq), -(-Skv // bkv))
+        need(tuple(block_mask.shape) == want, f"block_mask must be {want} (expand() views broadcast), got "
+                                              f"{tuple(block_mask.shape)}")
+
+
 def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False, block_mask=None,
         mask_block=(64, 256), page_table=None, page_size=16, seq_len_kv=None, softmax_scale=None,
         lazy_rescale_log2=8.0, out=None, out_dtype="bf16", sfs_o=None, stream=None):
@@ -203,6 +236,8 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
     for s in (sfs_q, sfs_k, sfs_v, sfs_p, sfs_o):
         if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()):
             raise ValueError("scale factors must be contiguous float32")
+    _check_shapes(q, k, v, out, sfs_q, sfs_k, sfs_v, sfs_p, sfs_o, block_mask, mask_block, page_table, page_size,
+                  Skv, Hkv)
     p = FmhaFwdParams()
     p.struct_size = ctypes.sizeof(FmhaFwdParams)
     p.B, p.Sq, p.Skv, p.Hq, p.Hkv, p.D = B, Sq, Skv, Hq, Hkv, D

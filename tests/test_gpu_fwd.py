@@ -385,3 +385,30 @@ def test_full_workload_sampled_rows(name, heads, rows, workload_cache):
     else:
         for b, h in heads:
             Hn.assert_parity(g[b, :, h], (ref[0][b, :, h], ref[1][b, :, h]), unq[b, :, h], what=f"{name} b={b} h={h}")
+
+
+def test_binding_rejects_mismatched_shapes():
+    # every extent the kernels index with is checked before the launch
+    import fmha_fwd_amd as F
+    dev = "cuda"
+    q = torch.zeros((1, 64, 4, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device=dev)
+    kq = torch.zeros((1, 64, 2, 128), dtype=torch.float8_e4m3fn, device=dev)
+    sv = torch.ones((1, 2, 1), dtype=torch.float32, device=dev)
+    bad = [
+        dict(k=torch.zeros((1, 64, 2, 192), dtype=torch.bfloat16, device=dev)),     # head dim differs
+        dict(v=torch.zeros((1, 32, 2, 128), dtype=torch.float8_e4m3fn, device=dev)),  # v shorter than k
+        dict(out=torch.zeros((1, 64, 4, 64), dtype=torch.bfloat16, device=dev)),
+        dict(sfs_v=torch.ones((1, 2, 2), dtype=torch.float32, device=dev)),
+        dict(sfs_p=torch.ones((2,), dtype=torch.float32, device=dev)),
+        dict(block_mask=torch.ones((1, 4, 1, 2), dtype=torch.uint8, device=dev)),
+    ]
+    for kw in bad:
+        args = dict(k=k, v=kq, sfs_v=sv)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            F.fwd(q, args.pop("k"), args.pop("v"), **args)
+    pt = torch.zeros((1, 3), dtype=torch.int32, device=dev)
+    pool = torch.zeros((8, 16, 2, 128), dtype=torch.float8_e4m3fn, device=dev)
+    with pytest.raises(ValueError):  # 3 pages of 16 tokens cannot hold 64 keys
+        F.fwd(q, pool, pool, sfs_k=sv, sfs_v=sv, page_table=pt, seq_len_kv=64)
