@@ -137,6 +137,8 @@ def quantize_blocks(x, dtype="e4m3", *, codes=None, scales=None, stream=None):
         scales = torch.empty((B, H, (S + 63) // 64), dtype=torch.float32, device=x.device)
     if not scales.is_contiguous():
         raise ValueError("scales must be contiguous")
+    if tuple(codes.shape) != (B, S, H, D) or tuple(scales.shape) != (B, H, (S + 63) // 64):
+        raise ValueError(f"codes must be {(B, S, H, D)} and scales {(B, H, (S + 63) // 64)}")
     xt, ct = _tensor(x), _tensor(codes)
     _check(lib_handle().fmha_quantize_blocks(ctypes.byref(xt), ctypes.byref(ct), scales.data_ptr(),
                                              B, S, H, D, 64, _stream(stream)))
@@ -167,6 +169,8 @@ def quantize_nvfp4(x, *, codes=None, block_scales=None, token_scales=None, strea
             raise ValueError("codes / block_scales must be 2-D byte tensors with a contiguous last dimension")
     if not token_scales.is_contiguous() or token_scales.dtype != torch.float32:
         raise ValueError("token_scales must be a contiguous fp32 tensor")
+    if tuple(codes.shape) != (M, K // 2) or tuple(block_scales.shape) != (M, K // 16) or token_scales.numel() != M:
+        raise ValueError(f"codes must be {(M, K // 2)}, block_scales {(M, K // 16)}, token_scales ({M},)")
     _check(lib_handle().fmha_quantize_nvfp4(x.data_ptr(), x.stride(0), M, K, codes.data_ptr(), codes.stride(0),
                                             block_scales.data_ptr(), block_scales.stride(0),
                                             token_scales.data_ptr(), _stream(stream)))

@@ -110,3 +110,15 @@ def test_full_size_workload_sampled_rows():
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(9).choice(M, 254, replace=False)]))
     _check(x_all[rows], c.cpu().numpy()[rows], sf.view(torch.uint8).cpu().numpy()[rows], ts.cpu().numpy()[rows])
+
+
+def test_binding_rejects_mismatched_outputs():
+    import fmha_fwd_amd as F
+    x = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        F.quantize_nvfp4(x, codes=torch.zeros((8, 64), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        F.quantize_nvfp4(x, token_scales=torch.zeros((4,), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        F.quantize_blocks(torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda"), "e4m3",
+                          scales=torch.zeros((1, 2, 2), dtype=torch.float32, device="cuda"))
