@@ -216,7 +216,7 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
                 "fwd: no kernel for (q, k, v) = (%d, %d, %d) with scales (q %d, k %d, v %d); supported: "
                 "bf16/bf16/bf16 unscaled, int8/int8/e4m3 [q,k,v], bf16/bf16/e4m3 [v or none], "
                 "e4m3/e4m3/e4m3 [q,k,v], bf16/e4m3/e4m3 [k,v]; with D=192 only int8/int8/e4m3 and e4m3/e4m3/e4m3 "
-                "[q,k,v] and bf16/bf16/e4m3 [v], without a block mask or page table",
+                "[q,k,v], bf16/bf16/e4m3 [v] and bf16/bf16/bf16 unscaled, without a block mask or page table",
                 (int)p->q.dtype, (int)p->k.dtype, (int)p->v.dtype, sb[0], sb[1], sb[2]);
   if (empty) return ok();
 

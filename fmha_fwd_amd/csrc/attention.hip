@@ -1031,14 +1031,16 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
 
 bool fwd_supported(const FwdKey& k) {
   if (k.D == 192) {
-    // head dim 192: dense or causal, 8-bit Q and K, or bf16 Q and K with a
-    // scaled E4M3 V (the DiT formats); bf16 Q and K read a quarter of the K
-    // operands at a time so that Q, O and the reads fit two wavefronts per
-    // SIMD
+    // head dim 192: dense or causal, 8-bit Q and K, bf16 Q and K with a
+    // scaled E4M3 V (the DiT formats), or all bf16; bf16 Q and K read a
+    // quarter of the K operands at a time so that Q, O and the reads fit two
+    // wavefronts per SIMD (all-bf16 K and V tiles take 100 KB of LDS: one
+    // workgroup per CU)
     if (k.masked || k.paged) return false;
     if (k.qf == FMT_INT8 && k.kf == FMT_INT8 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
     if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
     if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_E4M3) return !k.q_scaled && !k.k_scaled && k.v_scaled;
+    if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_BF16) return !k.q_scaled && !k.k_scaled && !k.v_scaled;
     return false;
   }
   if (k.D != 128) return false;
@@ -1081,6 +1083,8 @@ hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
   if (k.D == 192) {
     // no heads packed inside a wave (that needs the RP instances); whole-wave
     // head packing is a run-time choice of the same instance
+    if (k.qf == FMT_BF16 && k.vf == FMT_BF16)
+      return launch<Cfg<FMT_BF16, FMT_BF16, FMT_BF16, false, false, false, false, false, kDenseWaves, false, 192>>(a, s);
     if (k.qf == FMT_BF16)
       return launch<Cfg<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, true, false, false, kDenseWaves, false, 192>>(a, s);
     if (k.qf == FMT_INT8)

@@ -118,8 +118,8 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes,
 typedef struct {
   uint32_t struct_size;
   int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128, or 192 for the int8 / E4M3
-                                      keys and bf16/bf16/e4m3 [v], without
-                                      block mask or page table;
+                                      keys, bf16/bf16/e4m3 [v] and all-bf16,
+                                      without block mask or page table;
                                       Hq % Hkv == 0; query head h reads
                                       key/value head h / (Hq / Hkv) */
   /* q: [B, Sq, Hq, D]; o: [B, Sq, Hq, D] bf16 or E4M3 (written).

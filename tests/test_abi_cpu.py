@@ -88,8 +88,8 @@ def _call(lib, p):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(D=64), F.FMHA_ERR_UNSUPPORTED, "D=64"),
-    (dict(D=192, v=_tensor(F.FMHA_DT_BF16), sfs_v=0, sage_block_v=0), F.FMHA_ERR_UNSUPPORTED,
-     "with D=192 only"),                                           # all-bf16 at head dim 192
+    (dict(D=192, k=_tensor(F.FMHA_DT_E4M3), sfs_k=FAKE, sage_block_k=64), F.FMHA_ERR_UNSUPPORTED,
+     "with D=192 only"),                                           # bf16 Q x E4M3 K at head dim 192
     (dict(D=192, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), sfs_q=FAKE, sfs_k=FAKE, sage_block_q=64,
           sage_block_k=64, block_mask=FAKE, mask_block_q=64, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "no kernel"),
     (dict(Hq=6, Hkv=4), F.FMHA_ERR_INVALID, "multiple"),

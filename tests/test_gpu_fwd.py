@@ -326,12 +326,13 @@ def test_small_causal_gqa_packed(S):
                                                       ("gqa", 1, 4, 2, False, 0), ("gqa", 2, 8, 2, True, 100),
                                                       ("dit_i8", 2, 2, 1, True, 0), ("dit", 1, 2, 2, False, 0),
                                                       ("dit", 2, 4, 2, True, 0), ("gqa", 2, 16, 2, True, 5),
-                                                      ("dit", 1, 16, 2, False, 3)])
+                                                      ("dit", 1, 16, 2, False, 3), ("tiny", 1, 2, 2, False, 0),
+                                                      ("tiny", 2, 4, 2, True, 0)])
 @pytest.mark.parametrize("S", [1, 65, 320, 1000])
 def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
-    # head dim 192 with 8-bit Q and K, or bf16 Q and K with E4M3 V: dense,
-    # causal, GQA (whole-wave head packing for the causal groups), a query
-    # chunk, ragged tails
+    # head dim 192 with 8-bit Q and K, bf16 Q and K with E4M3 V, or all bf16:
+    # dense, causal, GQA (whole-wave head packing for the causal groups), a
+    # query chunk, ragged tails
     if sq >= S:
         sq = 0
     _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv, causal=causal, sq=sq, D=192))
