@@ -41,6 +41,17 @@ relative distance flip_eps of such a boundary of |one-step change in w_j| *
 (share of w_j left after later rescales) * |V_j - O| / den: to first order,
 the most the output can move through such ties.  The output itself does not
 depend on flip_eps.
+
+``flip_eps="binary32"`` replaces the fixed relative distance by a per-pair
+bound on the error of a kernel that works in IEEE binary32: it accumulates
+q . k with at most D roundings (error <= gamma_D * sum_d |q_d k_d|, gamma_D =
+D u / (1 - D u), u = 2^-24, the standard bound for any summation order; a
+fused or integer accumulation is only more accurate), then rounds at most
+four more times in forming the exponent s2 - m - log2(sp) (the scale
+product, the running maximum, the log of sp and the fused multiply-add: at
+most 4 u (|s2| + |m| + |log2 sp|)), and evaluates 2^x to within 2 ulp
+(2^-22 relative).  The relative error of P is then at most ln 2 times the
+exponent error plus 2^-22, to first order.
 """
 import math
 
@@ -49,6 +60,18 @@ import numpy as np
 from .codecs import bf16_round64, e4m3_decode, e4m3_encode, e4m3_round, rounding_gap
 
 LOG2E = 1.0 / math.log(2.0)
+U32 = 2.0 ** -24  # unit roundoff of IEEE binary32
+
+
+def binary32_p_error(q, k, s, m, D, c, sp):
+    """Relative error bound of P = 2^(s - m) / sp for a binary32 kernel (see
+    the module docstring): s = c * (q . k) are the fp64 log2-domain scores of
+    the pairs (rows of q against rows of k), m the row's reference maximum."""
+    gamma = D * U32 / (1.0 - D * U32)
+    acc = c * gamma * (np.abs(q) @ np.abs(k).T)
+    with np.errstate(invalid="ignore"):
+        rnd = 4.0 * U32 * (np.abs(s) + np.abs(m)[:, None] + abs(math.log2(sp)))
+    return math.log(2.0) * (acc + rnd) + 2.0 ** -22
 
 
 def dequantize(codes, fmt, scales=None, block_tokens=64):
@@ -158,7 +181,12 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
         num += w @ vv
         den += w.sum(axis=1)
         if flip_eps is not None:
-            gap = np.where(vs, rounding_gap(p / sp, p_format, flip_eps) * sp, 0.0)
+            eps = flip_eps
+            if isinstance(flip_eps, str):
+                assert flip_eps == "binary32", flip_eps
+                eps = np.where(vs, binary32_p_error(q, k[cols], np.where(vs, s, 0.0), m, D,
+                                                    softmax_scale * LOG2E, sp), 0.0)
+            gap = np.where(vs, rounding_gap(p / sp, p_format, eps) * sp, 0.0)
             if gap.any():
                 ties.append((cols, gap, m.copy(), vv))
     with np.errstate(invalid="ignore", divide="ignore"):

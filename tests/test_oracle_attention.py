@@ -13,8 +13,9 @@ from oracle.codecs import e4m3_decode
 from oracle.quantize import quantize_blocks
 
 
-def _sdpa(qd, kd, vd, causal=False, block_mask=None, scale=None):
-    """torch's CPU scaled_dot_product_attention in fp64 (heads expanded for GQA)."""
+def _sdpa(qd, kd, vd, causal=False, block_mask=None, scale=None, mask_block_q=64, mask_block_kv=256):
+    """torch's CPU scaled_dot_product_attention in fp64 (heads expanded for GQA;
+    a block mask expanded to pairs by repeating each entry over its block)."""
     B, Sq, Hq, D = qd.shape
     Skv, Hkv = kd.shape[1], kd.shape[2]
     g = Hq // Hkv
@@ -28,7 +29,7 @@ def _sdpa(qd, kd, vd, causal=False, block_mask=None, scale=None):
         mask &= (j <= i + Skv - Sq)
     if block_mask is not None:
         bm = torch.from_numpy(block_mask != 0)
-        mask &= bm.repeat_interleave(64, 2)[:, :, :Sq].repeat_interleave(256, 3)[..., :Skv]
+        mask &= bm.repeat_interleave(mask_block_q, 2)[:, :, :Sq].repeat_interleave(mask_block_kv, 3)[..., :Skv]
     o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
     return o.permute(0, 2, 1, 3).numpy()
 
@@ -60,6 +61,29 @@ def test_unquantized_block_mask_matches_torch_sdpa():
         bm[:, :, qb, min(qb // 4, nkb - 1)] = 1  # every row keeps a block
     got = attention(qd, kd, vd, block_mask=bm)
     assert np.allclose(got, _sdpa(qd, kd, vd, block_mask=bm, scale=1 / math.sqrt(D)), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_block", [64, 192, 512])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_key_block_sizes_match_torch_sdpa(kv_block, causal):
+    """expand_block_mask at key-block sizes other than 256 (the sizes the
+    kernel accepts: positive multiples of 64), with ragged last blocks on both
+    axes, against torch's attention under the pair mask built by repetition."""
+    B, Sq, Skv, H, D = 2, 200, 1100, 3, 8
+    rng = np.random.default_rng(kv_block + 7 * causal)
+    qd = rng.standard_normal((B, Sq, H, D)) * 2.0
+    kd = rng.standard_normal((B, Skv, H, D)) * 2.0
+    vd = rng.standard_normal((B, Skv, H, D))
+    nqb, nkb = -(-Sq // 64), -(-Skv // kv_block)
+    bm = (rng.random((B, H, nqb, nkb)) < 0.4).astype(np.uint8)
+    bm[..., nkb - 1] = 1  # every row keeps its last key block (visible under bottom-right causal)
+    for mode in ("lazy", "exact"):
+        got = attention(qd, kd, vd, block_mask=bm, causal=causal, mode=mode, mask_block_kv=kv_block)
+        ref = _sdpa(qd, kd, vd, causal=causal, block_mask=bm, scale=1 / math.sqrt(D), mask_block_kv=kv_block)
+        assert np.allclose(got, ref, rtol=1e-10, atol=1e-12), (kv_block, mode)
+    # a different key-block size is a different mask: the pin can tell them apart
+    other = attention(qd, kd, vd, block_mask=bm, causal=causal, mode="exact", mask_block_kv=2 * kv_block)
+    assert not np.allclose(other, ref, rtol=1e-6, atol=1e-8)
 
 
 def test_softmax_scale_is_applied():
@@ -276,3 +300,40 @@ def test_output_e4m3_hand_values():
     assert np.array_equal(got[0, :, 0, 0], want) and np.array_equal(got[0, :, 1, 0], want)
     # no scale: the values themselves
     assert np.array_equal(output_e4m3(o[:, :, :1] / so[0])[0, :, 0, 0], want)
+
+
+@pytest.mark.parametrize("p_format", ["e4m3", "bf16"])
+def test_binary32_bound_covers_a_binary32_evaluation(p_format):
+    """The per-pair binary32 bound against an independent binary32 evaluation
+    of the same attention (exact mode: scores by a float32 matrix product,
+    scale, maximum, subtraction and exp2 in float32, then the same P format).
+    Every output element lies within the bound of the fp64 result, the bound
+    is needed (some P values do round the other way), and it is tighter than a
+    fixed relative distance of 2^-12."""
+    from oracle.codecs import bf16_round64, e4m3_round
+    rng = np.random.default_rng(77)
+    n, Skv, D = 256, 4096, 128
+    # bf16-valued operands, exactly representable in float32
+    q = W_bf16(rng.standard_normal((1, n, 1, D)) * 1.5)
+    k = W_bf16(rng.standard_normal((1, Skv, 1, D)) * 1.5)
+    v = W_bf16(rng.standard_normal((1, Skv, 1, D)))
+    c = (1.0 / math.sqrt(D)) * (1.0 / math.log(2.0))
+    o, bound = attention(q, k, v, mode="exact", p_format=p_format, flip_eps="binary32")
+    s32 = (q[0, :, 0].astype(np.float32) @ k[0, :, 0].astype(np.float32).T) * np.float32(c)
+    m32 = s32.max(axis=1, keepdims=True)
+    p32 = np.exp2((s32 - m32).astype(np.float32)).astype(np.float64)
+    w = e4m3_round(p32) if p_format == "e4m3" else bf16_round64(p32)
+    o32 = (w @ v[0, :, 0]) / w.sum(axis=1, keepdims=True)
+    s64 = (q[0, :, 0] @ k[0, :, 0].T) * c
+    p64 = np.exp2(s64 - s64.max(axis=1, keepdims=True))
+    w64 = e4m3_round(p64) if p_format == "e4m3" else bf16_round64(p64)
+    flips = int((w != w64).sum())  # P values the binary32 evaluation rounds the other way
+    assert flips > 0, "no P rounded the other way: the case does not exercise the bound"
+    assert np.all(np.abs(o32 - o[0, :, 0]) <= bound[0, :, 0] + 1e-9)
+    _, fixed = attention(q, k, v, mode="exact", p_format=p_format, flip_eps=2.0 ** -12)
+    assert bound.sum() < fixed.sum()
+
+
+def W_bf16(x):
+    from fmha_fwd_amd.workloads import to_bf16_values
+    return to_bf16_values(np.asarray(x, dtype=np.float32)).astype(np.float64)
