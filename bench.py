@@ -57,58 +57,154 @@ def pair_count(spec, data):
     return spec.pairs()
 
 
-def cpu_baseline(spec, data, budget_s=12.0):
-    """The oracle (as it stands) on a bounded row sample of the workload."""
-    from oracle.attention import attention, dequantize
-    from oracle.quantize import quantize_blocks
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    h = 0
-    hk = h // (spec.Hq // spec.Hkv)
-    sub = lambda x, hh: x[:1, :, [hh]]
+        return 1
 
-    def operand(x, fmt, hh):
+
+def host_cores():
+    """Cores this process may run on (the CPU share of the box)."""
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(spec, data, budget_s=12.0, n_heads=6):
+    """The oracle (as it stands) on a bounded row sample of the workload:
+    rows of n_heads (batch, query head) pairs spread over the workload (the
+    first and the last head and random ones), each head's first, last and
+    tail-block rows first, then random rows, 64 at a time, round robin over
+    the heads until the time budget is spent.  Rows are independent, so the
+    sample is exact for the rows it covers."""
+    from oracle.attention import attention, dequantize
+    from oracle.quantize import quantize_blocks
+    rng = np.random.default_rng(0)
+    nq, group = spec.n_q, spec.Hq // spec.Hkv
+    heads = [(0, 0), (spec.B - 1, spec.Hq - 1)]
+    while len(heads) < min(n_heads, spec.B * spec.Hq):
+        bh = (int(rng.integers(spec.B)), int(rng.integers(spec.Hq)))
+        if bh not in heads:
+            heads.append(bh)
+
+    def operand(x, fmt, b, hh):
+        sub = x[b:b + 1, :, [hh]]
         if fmt == "bf16":
-            return sub(x, hh).astype(np.float64)
-        c, s = quantize_blocks(sub(x, hh), fmt)
+            return sub.astype(np.float64)
+        c, s = quantize_blocks(sub, fmt)
         return dequantize(c, fmt, s)
 
-    t0 = time.perf_counter()
-    qd = operand(data["q"], spec.q_fmt, h)
-    kd = operand(data["k"], spec.k_fmt, hk)
-    vd = operand(data["v"], spec.v_fmt, hk)
-    t_prep = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    rows_done, pairs_done, t_att = 0, 0, 0.0
-    bm = data.get("block_mask")
-    bm = None if bm is None else bm[:1, [h]]
-    nq = spec.n_q
-    while t_att < budget_s and rows_done < nq:
-        rows = np.sort(rng.choice(nq, size=min(64, nq), replace=False))
+    bm_all = data.get("block_mask")
+    first = np.unique(np.clip([0, 1, 63, 64, nq - 1, nq - 2, nq - 57, nq - 64, nq // 2], 0, nq - 1))
+    plan = []
+    for b, h in heads:
+        pool = np.setdiff1d(np.arange(nq), first)
+        plan.append([b, h, None, list(first) + list(rng.permutation(pool))])
+    t_prep, t_att, rows_done, pairs_done = 0.0, 0.0, 0, 0
+    i = 0
+    while t_att < budget_s and any(p[3] for p in plan):
+        entry = plan[i % len(plan)]
+        i += 1
+        b, h, ops, todo = entry
+        if not todo:
+            continue
+        if ops is None:
+            t0 = time.perf_counter()
+            ops = entry[2] = (operand(data["q"], spec.q_fmt, b, h), operand(data["k"], spec.k_fmt, b, h // group),
+                              operand(data["v"], spec.v_fmt, b, h // group))
+            t_prep += time.perf_counter() - t0
+        rows = np.sort(np.array(todo[:64]))
+        del todo[:64]
+        bm = None if bm_all is None else bm_all[b:b + 1, [h]]
         t0 = time.perf_counter()
-        attention(qd, kd, vd, causal=spec.causal, block_mask=bm, mode="lazy",
-                  p_format=spec.v_fmt, rows=rows, heads=[(0, 0)])
+        attention(*ops, causal=spec.causal, block_mask=bm, mode="lazy", p_format=spec.v_fmt, rows=rows,
+                  heads=[(0, 0)])
         t_att += time.perf_counter() - t0
         rows_done += len(rows)
         if spec.causal:
             pairs_done += int(np.minimum(rows + spec.S - nq + 1, spec.S).sum())
         elif bm is not None:
-            pairs_done += int(sum(bm[0, 0, r // 64].sum() * 256 for r in rows))
+            klen = np.minimum(256, spec.S - 256 * np.arange(bm.shape[3]))
+            pairs_done += int(sum((bm[0, 0, r // 64] != 0).astype(np.int64) @ klen for r in rows))
         else:
             pairs_done += len(rows) * spec.S
     flops = 4.0 * spec.D * pairs_done
-    rows_total = spec.B * spec.Hq * nq
-    return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "rows_per_s": rows_done / t_att,
+    return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "blas_threads": blas_threads(),
+            "kind": "oracle", "rows_per_s": rows_done / t_att,
             "extrapolated_full_s": 4.0 * spec.D * (pair_count(spec, data) or 0) / (flops / t_att),
-            "rows_total": rows_total,
-            "sample": f"{rows_done} random query rows of head 0 (batch 0), all {spec.S} keys each, lazy E4M3-P "
-                      f"oracle in fp64 numpy; operand dequantisation ({t_prep:.1f} s) not counted; "
-                      f"{t_att:.1f} s of CPU time",
+            "rows_total": spec.B * spec.Hq * nq,
+            "sample": f"{rows_done} query rows of {len(heads)} (batch, head) pairs {heads} (each head's first, last "
+                      f"and tail-block rows, then random rows), all their valid keys, lazy {spec.v_fmt}-P oracle "
+                      f"in fp64 numpy; operand dequantisation ({t_prep:.1f} s) not counted; {t_att:.1f} s of CPU "
+                      f"time",
             "seconds": round(t_att, 2)}
+
+
+class SclkSampler:
+    """Shader (GFX) clock read from the amdgpu sysfs files of the benchmarked
+    device while the timed steps run: hwmon's freq1_input (Hz), else the
+    level marked current in pp_dpm_sclk (MHz).  A background thread polls it
+    every few milliseconds; no subprocess."""
+
+    def __init__(self, torch, period_s=0.003):
+        import glob
+        import threading
+        self.samples, self.period, self.source = [], period_s, None
+        dirs = []
+        try:
+            pr = torch.cuda.get_device_properties(0)
+            dom, bus, dev = (getattr(pr, n, None) for n in ("pci_domain_id", "pci_bus_id", "pci_device_id"))
+            if bus is not None:
+                dirs = [f"/sys/bus/pci/devices/{dom or 0:04x}:{bus:02x}:{dev or 0:02x}.0"]
+        except Exception:  # pragma: no cover
+            pass
+        if not dirs or not os.path.isdir(dirs[0]):
+            cands = [d for d in glob.glob("/sys/class/drm/card*/device") if os.path.exists(d + "/pp_dpm_sclk")]
+            dirs = cands if len(set(map(os.path.realpath, cands))) == 1 else []
+        for d in dirs[:1]:
+            hw = sorted(glob.glob(d + "/hwmon/hwmon*/freq1_input"))
+            if hw:
+                self.source = (hw[0], 1e-9)
+            elif os.path.exists(d + "/pp_dpm_sclk"):
+                self.source = (d + "/pp_dpm_sclk", None)
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        path, scale = self.source
+        txt = open(path).read()
+        if scale is not None:
+            return float(txt.split()[0]) * scale
+        for line in txt.splitlines():
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().lower().split("mhz")[0]) * 1e-3
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self.read()
+                if v:
+                    self.samples.append(v)
+            except Exception:  # pragma: no cover
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.source is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"ghz_median": float(np.median(self.samples)), "ghz_min": float(np.min(self.samples)),
+                "ghz_max": float(np.max(self.samples)), "samples": len(self.samples), "source": self.source[0]}
 
 
 COPY_BYTES = 1 << 30
@@ -129,11 +225,6 @@ def nvfp4_source_hash():
 def nvfp4_cpu_baseline(x_rows_fn, M, K, budget_s=12.0):
     """The NVFP4 oracle (as it stands) on a bounded row sample."""
     from oracle.nvfp4 import quantize_nvfp4
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     rng = np.random.default_rng(0)
     rows_done, t = 0, 0.0
     while t < budget_s and rows_done < M:
@@ -143,7 +234,8 @@ def nvfp4_cpu_baseline(x_rows_fn, M, K, budget_s=12.0):
         quantize_nvfp4(x)
         t += time.perf_counter() - t0
         rows_done += 256
-    return {"value": nvfp4_bytes(rows_done, K) / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": nvfp4_bytes(rows_done, K) / t / 1e9, "unit": "GB/s", "cores": host_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
             "rows_per_s": rows_done / t, "extrapolated_full_s": M / (rows_done / t),
             "sample": f"{rows_done} rows (random 256-row groups) of the {M} x {K} matrix, NVFP4 oracle in numpy float32 emulation; "
                       f"{t:.1f} s of CPU time", "seconds": round(t, 2)}
@@ -322,11 +414,12 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler(torch) as sclk_sampler:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     q_ms = [e[0].elapsed_time(e[1]) for e in events]
     f_ms = [e[1].elapsed_time(e[2]) for e in events]
     ms_step = wall * 1e3 / args.steps
@@ -342,13 +435,15 @@ def main():
     achieved = flops / (fwd_ms * 1e-3) / 1e12
     quant_bytes = sum(x.numel() * 3 + s.numel() * 4 for _, x, _, _, s in quant)
 
-    traffic, sclk = None, None
+    traffic, sclk_counters = None, None
     tfile = os.path.join(ROOT, "profiles", f"fwd_{spec.name}_traffic.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("source_hash") == source_hash():
             traffic = t.get("bytes_per_launch")
-            sclk = t.get("sclk_ghz")
+            sclk_counters = t.get("sclk_ghz")
+    sclk_live = sclk_sampler.summary()
+    sclk = sclk_live["ghz_median"] if sclk_live else sclk_counters
 
     rec = {
         "metric": METRIC,
@@ -370,10 +465,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": "fmha_fwd", "frac_of_fp8_peak": achieved / PEAK["e4m3"],
-                     # shader clock measured under this kernel (counters), and the fraction of
-                     # the peak at that clock (the published peaks assume 2.4 GHz)
+                     # shader clock while the timed steps ran (sysfs, median of the samples; else
+                     # the counter record's), and the fraction of the peak at that clock (the
+                     # published peaks assume 2.4 GHz)
                      "sclk_ghz_measured": sclk,
-                     "frac_at_measured_sclk": None if sclk is None else achieved / (peak * sclk / 2.4)},
+                     "sclk_sysfs": sclk_live, "sclk_ghz_counters": sclk_counters,
+                     "frac_at_measured_sclk": None if sclk is None else achieved / (peak * min(sclk, 2.4) / 2.4)},
         "fwd_ms": fwd_ms,
         "fwd_ms_median": fwd_median,
         "fwd_ms_min": fwd_min,

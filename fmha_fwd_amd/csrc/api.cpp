@@ -165,6 +165,12 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
   if ((r = check_tensor("k", p->k, need_kv)) != FMHA_OK) return r;
   if ((r = check_tensor("v", p->v, need_kv)) != FMHA_OK) return r;
   if ((r = check_tensor("o", p->o, !empty)) != FMHA_OK) return r;
+  // K/V token rows must not overlap: the copies bound a tile's bytes by
+  // (tokens x token stride), so a token stride below one row (a broadcast
+  // view with stride 0, say) would read zeros instead of the rows.
+  if (need_kv && (p->k.stride_s < p->D || p->v.stride_s < p->D))
+    return fail(FMHA_ERR_INVALID, "fwd: k/v stride_s (%lld, %lld elements) is below one token row (D=%d)",
+                (long long)p->k.stride_s, (long long)p->v.stride_s, p->D);
 
   const int sb[3] = {p->sage_block_q, p->sage_block_k, p->sage_block_v};
   const void* sp[3] = {p->sfs_q, p->sfs_k, p->sfs_v};

@@ -85,13 +85,17 @@ __global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel_d192(Quant
   const float qmax = OUT == FMT_INT8 ? 127.0f : 448.0f;
   const bool live = amax_bits >= 0x0080u;  // amax >= 2^-126
   const float scale = live ? amax / qmax : 1.0f;   // correctly rounded division
+  // A dead block (amax below 2^-126) takes scale 1 and all-zero codes: code
+  // 0x00 also for negative zeros and negative subnormals, whose product with
+  // any multiplier would keep the sign (E4M3 0x80).
   const float inv = live ? qmax / amax : 0.0f;
   uint8_t* cb = a.codes + (int64_t)b * a.c_sb + (int64_t)h * a.c_sh;
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int c = lane + 64 * i;
     const int tok = tok0 + c / CPR;
-    if (tok < a.S) *(uint2*)(cb + (int64_t)tok * a.c_ss + 8 * (c % CPR)) = encode8<OUT>(v[i], inv);
+    const uint2 out = live ? encode8<OUT>(v[i], inv) : make_uint2(0, 0);
+    if (tok < a.S) *(uint2*)(cb + (int64_t)tok * a.c_ss + 8 * (c % CPR)) = out;
   }
   if (lane == 0) a.scales[bh * a.nblk + blk] = scale;
 }
@@ -140,36 +144,13 @@ __global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel(QuantArgs 
   const float qmax = OUT == FMT_INT8 ? 127.0f : 448.0f;
   const bool live = amax_bits >= 0x0080u;  // amax >= 2^-126
   const float scale = live ? amax / qmax : 1.0f;   // correctly rounded division
-  const float inv = live ? qmax / amax : 0.0f;
+  const float inv = live ? qmax / amax : 0.0f;  // dead blocks: all-zero codes (as above)
 
   uint8_t* cb = a.codes + (int64_t)b * a.c_sb + (int64_t)h * a.c_sh + (lane & 15) * 8;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int tok = tok0 + row0 + 4 * i;
-    uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    float y[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      y[2 * j] = __uint_as_float(w[j] << 16) * inv;
-      y[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * inv;
-    }
-    uint2 out;
-    if (OUT == FMT_E4M3) {
-      int p0 = pack_e4m3<false>(y[0], y[1], 0);
-      p0 = pack_e4m3<true>(y[2], y[3], p0);
-      int p1 = pack_e4m3<false>(y[4], y[5], 0);
-      p1 = pack_e4m3<true>(y[6], y[7], p1);
-      out = make_uint2((uint32_t)p0, (uint32_t)p1);
-    } else {
-      uint32_t p[2] = {0, 0};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int c = (int)__builtin_rintf(y[j]);
-        c = c > 127 ? 127 : (c < -127 ? -127 : c);
-        p[j >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (j & 3));
-      }
-      out = make_uint2(p[0], p[1]);
-    }
+    const uint2 out = live ? encode8<OUT>(v[i], inv) : make_uint2(0, 0);
     if (tok < a.S) *(uint2*)(cb + (int64_t)tok * a.c_ss) = out;
   }
   if (lane == 0) a.scales[bh * a.nblk + blk] = scale;

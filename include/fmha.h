@@ -126,7 +126,9 @@ typedef struct {
    * k, v contiguous-cache case: [B, Skv, Hkv, D].
    * k, v paged case (page_table != NULL): pools [num_pages, page_size, Hkv, D]
    * where stride_b is the stride between pages and stride_s the stride
-   * between the slots of one page. */
+   * between the slots of one page.  The token (slot) stride of k and v must
+   * be at least D elements (FMHA_ERR_INVALID otherwise: no broadcast or
+   * overlapping key/value rows). */
   fmha_tensor q, k, v, o;
   /* Per-block scale factors, fp32 [B, H, ceil(S / 64)] contiguous (H = Hq for
    * sfs_q, Hkv for sfs_k / sfs_v; S = Sq or Skv, counted in logical tokens),

@@ -10,11 +10,19 @@ from oracle.quantize import quantize_blocks as oracle_quantize
 TOL_MAXABS = 1.5e-2
 TOL_COS_Q = 0.999
 TOL_COS_U = 0.99
-# Relative distance from a P rounding boundary within which a binary32 kernel
-# may round the other way (scores accumulate in binary32: ~1e-5 relative at
-# the workloads' score magnitudes, exp2 adds ~1 ulp); see the oracle's
-# rounding-sensitivity bound.
-FLIP_EPS = 2.0 ** -12
+# Distance from a P rounding boundary within which a binary32 kernel may
+# round the other way: the oracle's per-pair bound for a kernel that
+# accumulates the scores in binary32 (at most D roundings), rounds at most
+# four more times in the exponent and evaluates exp2 within 2 ulp.
+FLIP_EPS = "binary32"
+# Elements over the max-abs bar that the P-rounding bound excuses: at most
+# five in ten thousand of those compared (measured up to 2.8e-4 on the E4M3
+# Q/K inputs with per-head deviations up to 2, none elsewhere), or one row's
+# worth in small cases.
+TIE_FRACTION = 5e-4
+TIE_FLOOR = 128
+# every parity comparison of the session, printed by the terminal summary
+RECORDS = []
 
 
 # ------------------------------------------------------------------ oracle side
@@ -136,9 +144,12 @@ def assert_parity(gpu, ref_and_bound, unq=None, what=""):
     method's own."""
     ref, bound = ref_and_bound
     r = compare(gpu, ref, bound)
+    r["tie_cap"] = int(max(TIE_FLOOR, TIE_FRACTION * r["n"]))
+    RECORDS.append((what, r))
     msg = f"{what}: {r}"
     assert np.all(np.isfinite(gpu)), msg
     assert r["n_bad"] == 0, msg
+    assert r["n_tie"] <= r["tie_cap"], msg
     assert r["cos"] >= TOL_COS_Q, msg
     if unq is not None:
         cu = cosine(gpu, unq)

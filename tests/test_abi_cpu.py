@@ -99,6 +99,12 @@ def _call(lib, p):
     (dict(q=_tensor(F.FMHA_DT_BF16, ptr=FAKE + 8)), F.FMHA_ERR_INVALID, "aligned"),
     (dict(q=_tensor(F.FMHA_DT_BF16, ptr=0)), F.FMHA_ERR_INVALID, "null"),
     (dict(k=_tensor(F.FMHA_DT_BF16, ss=100)), F.FMHA_ERR_INVALID, "stride_s"),
+    (dict(k=_tensor(F.FMHA_DT_BF16, ss=0)), F.FMHA_ERR_INVALID, "below one token row"),    # broadcast K
+    (dict(v=_tensor(F.FMHA_DT_E4M3, ss=0)), F.FMHA_ERR_INVALID, "below one token row"),    # broadcast V
+    (dict(k=_tensor(F.FMHA_DT_BF16, ss=64)), F.FMHA_ERR_INVALID, "below one token row"),   # rows overlap
+    (dict(v=_tensor(F.FMHA_DT_E4M3, ss=112)), F.FMHA_ERR_INVALID, "below one token row"),
+    (dict(page_table=FAKE, page_size=16, num_pages=4, v=_tensor(F.FMHA_DT_E4M3, ss=16)), F.FMHA_ERR_INVALID,
+     "below one token row"),                                                               # paged slots overlap
     (dict(o=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "bf16 or e4m3"),
     (dict(sfs_o=FAKE), F.FMHA_ERR_INVALID, "sfs_o given"),
     (dict(o=_tensor(F.FMHA_DT_E4M3), sfs_o=FAKE + 2), F.FMHA_ERR_INVALID, "sfs_o misaligned"),

@@ -338,6 +338,51 @@ def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
     _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv, causal=causal, sq=sq, D=192))
 
 
+@pytest.mark.parametrize("base", ["dit", "gqa", "dit_i8", "sparse"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_block_scales_spanning_more_than_2_64(base, causal):
+    # V block scales more than 2^64 apart: the kernel then keeps O in fixed
+    # units and adds every sub-tile's product with its own scale (the slow
+    # V-reference path).  Block 1 of V is scaled by 2^-70 before quantisation
+    # (exact: the codes stay the same, the block scale moves by 2^-70) and
+    # block 3 by 4.
+    spec = W.small_spec(base, 320, B=1, Hq=4, Hkv=2, causal=causal)
+    print(f"fwd {spec} with V block scales spanning 2^72", flush=True)
+    data = W.generate(spec)
+    v = data["v"].copy()
+    v[:, 64:128] *= np.float32(2.0 ** -70)
+    v[:, 192:256] *= np.float32(4.0)
+    data["v"] = v
+    gpu, t = Hn.gpu_run(spec, data)
+    sv = t["sfs_v"].cpu().numpy()
+    assert sv.max() > sv.min() * 2.0 ** 64
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(gpu, Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data),
+                     what=f"V scales beyond 2^64 {base}")
+
+
+@pytest.mark.parametrize("S,causal", [(1, False), (320, False), (300, True), (1000, False)])
+def test_unscaled_e4m3_v(S, causal):
+    # bf16 Q and K with E4M3 V codes and no V scale (sage_block_v = 0): V is
+    # encoded directly (nearest-even, saturating) and read as its E4M3 values
+    import fmha_fwd_amd as F
+    from oracle.codecs import e4m3_decode, e4m3_encode
+    from oracle.attention import attention
+    spec = W.small_spec("dit", S, B=2, Hq=4, Hkv=2, causal=causal)
+    print(f"fwd {spec} with an unscaled E4M3 V", flush=True)
+    data = W.generate(spec)
+    vcodes = e4m3_encode(data["v"].astype(np.float64) * 3.0)  # values up to ~15: normals and subnormals
+    q, k = Hn.to_gpu_bf16(data["q"]), Hn.to_gpu_bf16(data["k"])
+    v = torch.from_numpy(vcodes).cuda().view(torch.float8_e4m3fn)
+    o = F.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    gpu = o.float().cpu().numpy()
+    qd, kd, vd = (data["q"].astype(np.float64), data["k"].astype(np.float64), e4m3_decode(vcodes))
+    ref = attention(qd, kd, vd, causal=causal, mode="lazy", p_format="e4m3", flip_eps=Hn.FLIP_EPS)
+    unq = attention(qd, kd, vd, causal=causal, mode="exact", p_format=None)
+    Hn.assert_parity(gpu, ref, unq, what=f"unscaled e4m3 V S={S}")
+
+
 def test_deterministic():
     spec = W.small_spec("gqa", 700, B=1, Hq=8, Hkv=2, causal=True)
     data = W.generate(spec)

@@ -105,3 +105,26 @@ def test_head_dim_192_bit_exact(fmt, shape):
     x = _bf16(x)
     _, c, s = _gpu_quant(x, fmt)
     _check(x, fmt, c, s)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+@pytest.mark.parametrize("d", [128, 192])
+def test_dead_blocks_with_negative_zeros_and_subnormals(fmt, d):
+    """A block whose amax is below 2^-126 takes scale 1 and code 0x00 for
+    every element, also for -0.0 and negative subnormals (whose sign an E4M3
+    encoding of x * 0 would keep as 0x80)."""
+    print(f"quantize dead blocks {fmt} d{d}", flush=True)
+    rng = np.random.default_rng(11 + d)
+    x = rng.standard_normal((1, 256 + 37, 2, d)).astype(np.float32)
+    x[0, 0:64] = -0.0                                                      # all negative zeros
+    x[0, 64:128] = np.where(rng.random((64, 2, d)) < 0.5, -0.0, 0.0)       # mixed signed zeros
+    tiny = np.float32(2.0 ** -130) * rng.integers(1, 8, (64, 2, d)).astype(np.float32)
+    x[0, 128:192] = np.where(rng.random((64, 2, d)) < 0.5, -tiny, tiny)    # signed bf16 subnormals
+    x[0, 192:256] = -np.float32(2.0 ** -133)                               # the smallest negative subnormal
+    x[0, 256:] = np.where(rng.random((37, 2, d)) < 0.5, -0.0, np.float32(-2.0 ** -127))  # dead ragged tail
+    x = _bf16(x)
+    assert np.signbit(x[0, 0:64]).all() and (x[0, 128:192] < 0).any()
+    _, c, s = _gpu_quant(x, fmt)
+    _check(x, fmt, c, s)
+    assert not c.view(np.uint8).any(), "dead blocks must hold code 0x00 only"
+    assert (s == 1.0).all()
