@@ -219,9 +219,8 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
 
     q: [B, Sq, Hq, D] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, D],
     or with page_table (int32 [B, pages]) pools [num_pages, page_size, Hkv, D]
-    and seq_len_kv giving Skv.  D = 128, or 192 for int8 / E4M3 Q and K,
-    bf16 Q and K with a scaled E4M3 V, or all bf16, without block mask or
-    page table.  sfs_*: fp32 [B, H, ceil(S/64)] block
+    and seq_len_kv giving Skv.  D = 128 or 192 (at 192 a bf16 Q and K with
+    an E4M3 V need its scale).  sfs_*: fp32 [B, H, ceil(S/64)] block
     scales.
     block_mask: uint8 [B, Hq, ceil(Sq/64), ceil(Skv/256)] (strides honoured;
     last dim contiguous).

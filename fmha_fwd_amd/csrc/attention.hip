@@ -105,8 +105,13 @@ struct Cfg {
   // lane's head, Q scale and P scale are its own (two more live registers)
   static constexpr bool RP = RP_;
   static constexpr int MT = QF;                                  // QK operand format
-  static constexpr int WPE =
-      MT == FMT_BF16 || MASKED || PAGED || RP || D != 128 ? FMHA_WAVES_PER_EU_BF16 : FMHA_WAVES_PER_EU_8BIT;
+  // (head dim 192 with a block mask, paged K/V or E4M3 K widened for a bf16
+  // Q: one wavefront per SIMD, all 512 registers; their LDS tiles allow no
+  // more than four wavefronts per CU anyway)
+  static constexpr int WPE = D != 128 && (MASKED || PAGED || (MT == FMT_BF16 && KF == FMT_E4M3))
+                                 ? 1
+                                 : MT == FMT_BF16 || MASKED || PAGED || RP || D != 128 ? FMHA_WAVES_PER_EU_BF16
+                                                                                      : FMHA_WAVES_PER_EU_8BIT;
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
@@ -1031,16 +1036,18 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
 
 bool fwd_supported(const FwdKey& k) {
   if (k.D == 192) {
-    // head dim 192: dense or causal, 8-bit Q and K, bf16 Q and K with a
-    // scaled E4M3 V (the DiT formats), or all bf16; bf16 Q and K read a
-    // quarter of the K operands at a time so that Q, O and the reads fit two
-    // wavefronts per SIMD (all-bf16 K and V tiles take 100 KB of LDS: one
-    // workgroup per CU)
-    if (k.masked || k.paged) return false;
+    // head dim 192: 8-bit Q and K, bf16 Q and K with a scaled E4M3 V (the
+    // DiT formats), all bf16, and bf16 Q with scaled E4M3 K and V (the
+    // block-sparse format); dense, causal, block-masked or paged.  bf16 Q and
+    // K read a quarter of the K operands at a time so that Q, O and the reads
+    // fit two wavefronts per SIMD (all-bf16 K and V tiles take 100 KB of LDS:
+    // one workgroup per CU); masked, paged and widened-K instances run one
+    // wavefront per SIMD
     if (k.qf == FMT_INT8 && k.kf == FMT_INT8 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
     if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
     if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_E4M3) return !k.q_scaled && !k.k_scaled && k.v_scaled;
     if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_BF16) return !k.q_scaled && !k.k_scaled && !k.v_scaled;
+    if (k.qf == FMT_BF16 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return !k.q_scaled && k.k_scaled && k.v_scaled;
     return false;
   }
   if (k.D != 128) return false;
@@ -1078,18 +1085,31 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
   return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves>>(a, s);
 }
 
+// Head dim 192: dense / causal (with whole-wave head packing as a run-time
+// choice), block-masked, paged, or both; no heads packed inside a wave (that
+// needs the RP instances).
+template <int QF, int KF, int VF, bool QS, bool KS, bool VS>
+static hipError_t dispatch_d192(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
+  if (k.masked) {
+    if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, true, true, 2, false, 192>>(a, s);
+    return launch<Cfg<QF, KF, VF, QS, KS, VS, true, false, 2, false, 192>>(a, s);
+  }
+  if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves, false, 192>>(a, s);
+  return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves, false, 192>>(a, s);
+}
+
 hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
   if (!fwd_supported(k)) return hipErrorInvalidValue;
   if (k.D == 192) {
-    // no heads packed inside a wave (that needs the RP instances); whole-wave
-    // head packing is a run-time choice of the same instance
     if (k.qf == FMT_BF16 && k.vf == FMT_BF16)
-      return launch<Cfg<FMT_BF16, FMT_BF16, FMT_BF16, false, false, false, false, false, kDenseWaves, false, 192>>(a, s);
+      return dispatch_d192<FMT_BF16, FMT_BF16, FMT_BF16, false, false, false>(k, a, s);
+    if (k.qf == FMT_BF16 && k.kf == FMT_BF16)
+      return dispatch_d192<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, true>(k, a, s);
     if (k.qf == FMT_BF16)
-      return launch<Cfg<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, true, false, false, kDenseWaves, false, 192>>(a, s);
+      return dispatch_d192<FMT_BF16, FMT_E4M3, FMT_E4M3, false, true, true>(k, a, s);
     if (k.qf == FMT_INT8)
-      return launch<Cfg<FMT_INT8, FMT_INT8, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);
-    return launch<Cfg<FMT_E4M3, FMT_E4M3, FMT_E4M3, true, true, true, false, false, kDenseWaves, false, 192>>(a, s);
+      return dispatch_d192<FMT_INT8, FMT_INT8, FMT_E4M3, true, true, true>(k, a, s);
+    return dispatch_d192<FMT_E4M3, FMT_E4M3, FMT_E4M3, true, true, true>(k, a, s);
   }
   if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_BF16)
     return dispatch_layout<FMT_BF16, FMT_BF16, FMT_BF16, false, false, false>(k, a, s);

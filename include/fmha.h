@@ -117,11 +117,10 @@ int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes,
  */
 typedef struct {
   uint32_t struct_size;
-  int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128, or 192 for the int8 / E4M3
-                                      keys, bf16/bf16/e4m3 [v] and all-bf16,
-                                      without block mask or page table;
-                                      Hq % Hkv == 0; query head h reads
-                                      key/value head h / (Hq / Hkv) */
+  int32_t B, Sq, Skv, Hq, Hkv, D;  /* D == 128 or 192 (at 192, bf16/bf16/e4m3
+                                      needs the V scale); Hq % Hkv == 0; query
+                                      head h reads key/value head
+                                      h / (Hq / Hkv) */
   /* q: [B, Sq, Hq, D]; o: [B, Sq, Hq, D] bf16 or E4M3 (written).
    * k, v contiguous-cache case: [B, Skv, Hkv, D].
    * k, v paged case (page_table != NULL): pools [num_pages, page_size, Hkv, D]

@@ -88,10 +88,10 @@ def _call(lib, p):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(D=64), F.FMHA_ERR_UNSUPPORTED, "D=64"),
-    (dict(D=192, k=_tensor(F.FMHA_DT_E4M3), sfs_k=FAKE, sage_block_k=64), F.FMHA_ERR_UNSUPPORTED,
-     "with D=192 only"),                                           # bf16 Q x E4M3 K at head dim 192
-    (dict(D=192, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), sfs_q=FAKE, sfs_k=FAKE, sage_block_q=64,
-          sage_block_k=64, block_mask=FAKE, mask_block_q=64, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(D=192, sfs_v=None, sage_block_v=0), F.FMHA_ERR_UNSUPPORTED,
+     "with D=192 the same except"),                                # bf16/bf16/e4m3 without V scale at 192
+    (dict(D=192, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), sfs_k=FAKE, sage_block_k=64,
+          block_mask=FAKE, mask_block_q=64, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "no kernel"),  # unscaled E4M3 Q
     (dict(Hq=6, Hkv=4), F.FMHA_ERR_INVALID, "multiple"),
     (dict(Hkv=0), F.FMHA_ERR_INVALID, "Hkv"),
     (dict(Sq=-1), F.FMHA_ERR_INVALID, "negative"),

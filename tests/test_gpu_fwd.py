@@ -383,6 +383,20 @@ def test_unscaled_e4m3_v(S, causal):
     Hn.assert_parity(gpu, ref, unq, what=f"unscaled e4m3 V S={S}")
 
 
+@pytest.mark.parametrize("base", ["sparse", "tiny", "dit", "dit_i8", "gqa"])
+@pytest.mark.parametrize("masked,paged", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("S,causal", [(300, False), (700, True)])
+def test_head_dim_192_masked_or_paged(base, masked, paged, S, causal):
+    # head dim 192 with a block mask and/or paged K/V for every format, incl.
+    # bf16 Q x E4M3 K (the block-sparse format, also dense)
+    _run_small(W.small_spec(base, S, B=2, Hq=4, Hkv=2, masked=masked, paged=paged, causal=causal, D=192))
+
+
+@pytest.mark.parametrize("S,causal", [(1, False), (130, True), (1000, False)])
+def test_head_dim_192_bf16_q_e4m3_k_dense(S, causal):
+    _run_small(W.small_spec("sparse", S, B=1, Hq=4, Hkv=2, masked=False, paged=False, causal=causal, D=192))
+
+
 def test_deterministic():
     spec = W.small_spec("gqa", 700, B=1, Hq=8, Hkv=2, causal=True)
     data = W.generate(spec)
@@ -403,6 +417,7 @@ FULL = [
     ("dit_i8_d192", [(0, 0), (0, 23)], "sample"),
     ("gqa_d192", [(0, 0), (1, 63)], "sample"),
     ("dit_d192", [(0, 0), (0, 39)], "sample"),
+    ("sparse_d192", [(0, 0), (3, 31)], "sample"),
 ]
 
 
