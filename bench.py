@@ -207,6 +207,7 @@ class SclkSampler:
                 "ghz_max": float(np.max(self.samples)), "samples": len(self.samples), "source": self.source[0]}
 
 
+SCLK_MIN_SAMPLES = 10  # sysfs clock readings needed before a median is reported
 COPY_BYTES = 1 << 30
 NVFP4_METRIC = "per-token NVFP4 quantisation GB/s (algorithmic bytes: 2 read + 0.5 + 1/16 written per element, 4 per token)"
 
@@ -443,6 +444,11 @@ def main():
             traffic = t.get("bytes_per_launch")
             sclk_counters = t.get("sclk_ghz")
     sclk_live = sclk_sampler.summary()
+    # sysfs reports an average that lags the shader clock: a timed region
+    # shorter than SCLK_MIN_SAMPLES readings (or with idle gaps) reads low, so
+    # then only the counter-derived clock of the profiles is used
+    if sclk_live is not None and sclk_live["samples"] < SCLK_MIN_SAMPLES:
+        sclk_live = None
     sclk = sclk_live["ghz_median"] if sclk_live else sclk_counters
 
     rec = {

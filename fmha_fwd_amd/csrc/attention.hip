@@ -95,10 +95,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Keys per LDS tile of the dense 8-bit-QK instances: 64 (one sub-tile per
+// barrier) or 128 (two sub-tiles per barrier, copied one tile ahead; twice
+// the LDS, so two wavefronts per SIMD instead of three).
+#ifndef FMHA_KV_TILE_8BIT
+#define FMHA_KV_TILE_8BIT 64
+#endif
+
 template <int QF_, int KF_, int VF_, bool QS_, bool KS_, bool VS_, bool MASKED_, bool PAGED_, int NW_,
-          bool RP_ = false, int D_ = 128>
+          bool RP_ = false, int D_ = 128, int KT_ = 64>
 struct Cfg {
   static constexpr int QF = QF_, KF = KF_, VF = VF_, NW = NW_;
+  static constexpr int KT = KT_, SUB = KT_ / 64;  // keys per LDS tile, sub-tiles per tile
+  static_assert(KT_ == 64 || ((KT_ == 128 || KT_ == 256) && !MASKED_ && !PAGED_ && !RP_), "larger tiles: dense only");
   static constexpr int D = D_, ND = D / 32;  // head dim; 32-row d-tiles of O^T
   static constexpr bool QS = QS_, KS = KS_, VS = VS_, MASKED = MASKED_, PAGED = PAGED_;
   // RP: heads packed inside a wave (fewer than 32 rows per head), so a
@@ -110,8 +119,9 @@ struct Cfg {
   // more than four wavefronts per CU anyway)
   static constexpr int WPE = D != 128 && (MASKED || PAGED || (MT == FMT_BF16 && KF == FMT_E4M3))
                                  ? 1
-                                 : MT == FMT_BF16 || MASKED || PAGED || RP || D != 128 ? FMHA_WAVES_PER_EU_BF16
-                                                                                      : FMHA_WAVES_PER_EU_8BIT;
+                             : MT == FMT_BF16 || MASKED || PAGED || RP || D != 128 || KT_ != 64
+                                 ? FMHA_WAVES_PER_EU_BF16
+                                 : FMHA_WAVES_PER_EU_8BIT;
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
@@ -125,7 +135,7 @@ struct Cfg {
   // 4 (10 or 14), so the 8 rows of a transposing read land on 8 distinct even
   // chunks and their neighbours (chunk c + 1) on the odd ones.
   static constexpr int KP = KROW + 16, VP = VF == FMT_BF16 ? VROW + 16 : VROW + 32;
-  static constexpr int K_BUF = kSub * KP, V_BUF = kSub * VP;
+  static constexpr int K_BUF = KT * KP, V_BUF = KT * VP;
   static constexpr int LDS_BYTES = 2 * (K_BUF + V_BUF);
   static constexpr int NT = NW * 64;
   static constexpr int K_CPR = KROW / 16, KP_CPR = KP / 16;      // 16-byte chunks per row
@@ -156,9 +166,29 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
   return x * per + min(x, r) + j;
 }
 
+// Persistent launch (build option, off by default): a grid of the resident
+// workgroup slots, each taking tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+// (gridDim.x a multiple of 8, so a workgroup's tiles stay in its XCD's range).
+#ifndef FMHA_PERSISTENT
+#define FMHA_PERSISTENT 0
+#endif
+#if FMHA_PERSISTENT
+#define FMHA_END_TILE goto tile_end
+#else
+#define FMHA_END_TILE return
+#endif
+
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE))) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+#if FMHA_PERSISTENT
+  for (int it = blockIdx.x; it < a.tiles; it += gridDim.x) {
+  const int lin = xcd_remap(it, a.tiles);
+#else
+  {
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+#endif
+  {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -177,7 +207,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   const bool pack = rows > 0;
   const int qtile = pack ? rows : 32 * C::NW;
   const int nqt = (a.Sq + qtile - 1) / qtile;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
   int qt = lin % nqt;
   if (a.causal) qt = nqt - 1 - qt;  // longest causal rows first
   const int rest = lin / nqt;
@@ -869,6 +898,59 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // SIMD being in another phase.  The copies of the next sub-tile are issued
   // early in the step and land while the current one is processed (paged:
   // its page numbers were read during the previous sub-tile).
+  if constexpr (C::SUB > 1) {
+    // ---- dense loop over tiles of SUB sub-tiles: the copies of tile T + 1
+    // are issued with the first sub-tile of tile T, one barrier per tile.
+    const int ntile = (n_sub + C::SUB - 1) / C::SUB;
+    if (ntile > 0) {
+      dma_k(0, 0, 0);
+      dma_v(0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;
+    auto sub_step = [&](int t, int T, auto u_tag, auto edge_tag, auto clamp_tag, auto direct_tag) {
+      constexpr int u = decltype(u_tag)::value;
+      const int bv = T & 1;
+      const lds_u8* kb = kbuf0 + bv * C::K_BUF + u * kSub * C::KP;
+      const lds_u8* vb = vbuf0 + bv * C::V_BUF + u * kSub * C::VP;
+      fetch_scales(t);
+      if (u == 0 && T + 1 < ntile) {
+        dma_k((T + 1) * C::SUB, bv ^ 1, 0);
+        dma_v((T + 1) * C::SUB, bv ^ 1, 0);
+      }
+      const SAcc<C::MT> acc = qk_raised(kb);
+      pv(softmax_p(acc, t, edge_tag, clamp_tag, direct_tag), vb, direct_tag);
+    };
+    auto run_tiles = [&](auto clamp_tag, auto direct_tag) {
+      // whole tiles valid for every pair, then the rest with per-pair masks
+      int T = 0;
+      for (; (T + 1) * C::SUB <= full_end; ++T) {
+        static_for<0, C::SUB>([&](auto u) { sub_step(T * C::SUB + u, T, u, std::false_type{}, clamp_tag, direct_tag); });
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        __syncthreads();
+      }
+      for (; T < ntile; ++T) {
+        static_for<0, C::SUB>([&](auto u) {
+          if (T * C::SUB + u < n_sub) sub_step(T * C::SUB + u, T, u, std::true_type{}, clamp_tag, direct_tag);
+        });
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
+    };
+    if constexpr (C::VS) {
+      if (clamp) {
+        if (v_direct) run_tiles(std::true_type{}, std::true_type{});
+        else run_tiles(std::true_type{}, std::false_type{});
+      } else {
+        if (v_direct) run_tiles(std::false_type{}, std::true_type{});
+        else run_tiles(std::false_type{}, std::false_type{});
+      }
+    } else {
+      if (clamp) run_tiles(std::true_type{}, std::true_type{});
+      else run_tiles(std::false_type{}, std::true_type{});
+    }
+  } else {
   int tc = next_sub(0);
   int tn = n_sub, pg_n = 0;
   if (tc < n_sub) {
@@ -956,12 +1038,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     else run(std::false_type{}, std::true_type{});
   }
 
+  }  // SUB == 1
+
   // ---- epilogue: O = num / den in bf16 (or E4M3); rows without a valid key give 0
   float dt;
   if constexpr (C::VF == FMT_E4M3) dt = den_acc[0];
   else dt = den + __shfl_xor(den, 32, 64);
   const float inv = dt > 0.0f ? sv_ref / dt : 0.0f;
-  if (qi >= a.Sq) return;
+  if (qi >= a.Sq) FMHA_END_TILE;
   uint8_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)qi * a.o_ss;
   if (a.o_fp8) {
     // E4M3 output: encode(O / sfs_o), nearest-even, saturating at +-448
@@ -978,7 +1062,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         *(int*)(op + 32 * d + 8 * a4 + 4 * g) = pk;
       }
     }
-    return;
+    FMHA_END_TILE;
   }
 #pragma unroll
   for (int d = 0; d < C::ND; ++d) {
@@ -992,8 +1076,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       *(uint2*)(op + 2 * dd) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
     }
   }
+  }  // tile
+#if FMHA_PERSISTENT
+  tile_end:
+  __syncthreads();
+#endif
+  }
 #endif
 }
+#undef FMHA_END_TILE
 
 // Rows per head of a packed workgroup (0: no packing).  Heads are packed
 // when the query range is causal or shorter than a workgroup tile; query
@@ -1020,14 +1111,24 @@ hipError_t launch(const FwdArgs& args, hipStream_t stream) {
   const int qtile = pack ? rows : 32 * C::NW;
   const int64_t tiles = (int64_t)((a.Sq + qtile - 1) / qtile) * a.Hq * a.B / (pack ? C::NW * (32 / rows) : 1);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  a.tiles = (int)tiles;
   dim3 grid((unsigned)tiles);
   const size_t lds = (size_t)C::LDS_BYTES;
   static bool configured = false;  // benign race: the attribute is idempotent
+  static int slots = 0;            // persistent launch: resident workgroups per device
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    if (FMHA_PERSISTENT) {
+      int dev = 0, cus = 0, per_cu = 0;
+      if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+      if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+      if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_kernel<C>, C::NT, lds)) != hipSuccess) return e;
+      slots = max(8, (cus * per_cu) / 8 * 8);
+    }
     configured = true;
   }
+  if (FMHA_PERSISTENT && tiles > slots) grid.x = (unsigned)slots;
   hipLaunchKernelGGL(fwd_kernel<C>, grid, dim3(C::NT), lds, stream, a);
   return hipGetLastError();
 }
@@ -1082,7 +1183,8 @@ static hipError_t dispatch_layout(const FwdKey& k, const FwdArgs& a, hipStream_t
     }
   }
   if (k.paged) return launch<Cfg<QF, KF, VF, QS, KS, VS, false, true, kDenseWaves>>(a, s);
-  return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves>>(a, s);
+  constexpr int KT = QF != FMT_BF16 ? FMHA_KV_TILE_8BIT : 64;
+  return launch<Cfg<QF, KF, VF, QS, KS, VS, false, false, kDenseWaves, false, 128, KT>>(a, s);
 }
 
 // Head dim 192: dense / causal (with whole-wave head packing as a run-time

@@ -59,6 +59,7 @@ struct FwdArgs {
   int kv_whole_rsrc;    // contiguous K/V of one (batch, head) span < 2^31 bytes: one buffer resource each
   int o_fp8;            // o is E4M3: encode(O / sfs_o[h])
   const float* sfs_o;   // [Hq] or null (= 1)
+  int tiles;            // set by the launcher: logical workgroup tiles of the launch
 };
 
 struct FwdKey {
