@@ -216,3 +216,52 @@ def nvfp4_activations(M, K, index=8, rows=None):
     x *= mag[idx][:, None]
     x[:, ch] *= np.float32(20.0)
     return to_bf16_values(x)
+
+
+SWEEP_BASES = ("tiny", "dit", "dit_i8", "gqa", "sparse")  # the five format combinations
+
+
+def sweep_case(i):
+    """Configuration i of a seeded random sweep: one of the five format
+    combinations, head dim 128 or 192, B 1-2, 1-2 KV heads with 1-8 query
+    heads each, 1-320 queries against 1-700 keys (ragged, either longer),
+    causal or not, and independently a block mask (64-query rows, key blocks
+    of 64-512, density 0.2-0.9, sometimes a query block with no key) and paged
+    K/V (pages of 16-256 tokens, a random page table over a pool with spare
+    pages).  Values are N(0, 1) scaled per head by U(0.5, 2), as bf16.
+
+    Returns (spec, data, mask_block_kv); data as `generate` returns it, with
+    q [B, Sq, Hq, D] and k, v [B, Skv, Hkv, D]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=(2000 + i,))))
+    base = SPECS[SWEEP_BASES[int(rng.integers(len(SWEEP_BASES)))]]
+    D = int(rng.choice([128, 192]))
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    group = int(rng.choice([1, 2, 4] if Hkv > 1 else [1, 2, 4, 8]))
+    Hq = Hkv * group
+    Skv = int(rng.integers(1, 701))
+    Sq = Skv if rng.random() < 0.25 else int(rng.integers(1, 321))
+    causal = bool(rng.random() < 0.5)
+    masked = bool(rng.random() < 0.35)
+    paged = bool(rng.random() < 0.35)
+    page_size = int(rng.choice([16, 32, 64, 128, 256]))
+    kvb = int(rng.choice([64, 128, 256, 512]))
+    spec = Spec(f"sweep{i}_{base.name}", 100 + i, B, Hq, Hkv, Skv, base.q_fmt, base.k_fmt, base.v_fmt,
+                causal, masked, paged, page_size, D=D, sq=Sq if Sq != Skv else 0)
+    sig = [rng.uniform(0.5, 2.0, H).astype(np.float32)[None, None, :, None] for H in (Hq, Hkv, Hkv)]
+    q = rng.standard_normal((B, Sq, Hq, D), dtype=np.float32) * sig[0]
+    k = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32) * sig[1]
+    v = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32) * sig[2]
+    data = {"q": to_bf16_values(q), "k": to_bf16_values(k), "v": to_bf16_values(v)}
+    if paged:
+        per_seq = -(-Skv // page_size)
+        pool = B * per_seq + int(rng.integers(0, 4))
+        data["page_table"] = rng.permutation(pool)[:B * per_seq].astype(np.int32).reshape(B, per_seq)
+    if masked:
+        nqb, nkb = -(-Sq // 64), -(-Skv // kvb)
+        mask = (rng.random((B, Hq, nqb, nkb)) < rng.uniform(0.2, 0.9)).astype(np.uint8)
+        if nqb > 1 and rng.random() < 0.5:
+            mask[:, :, int(rng.integers(nqb))] = 0
+        data["block_mask"] = mask
+    return spec, data, kvb
+

@@ -90,7 +90,7 @@ def gpu_run(spec, data, device="cuda", **fwd_kw):
     if spec.paged:
         pt = torch.from_numpy(data["page_table"]).to(device)
         ps = spec.page_size
-        n_pages = pt.numel()
+        n_pages = max(pt.numel(), int(data["page_table"].max()) + 1)  # pages no table entry names stay zero
         S = spec.S
         kpool = torch.zeros((n_pages, ps) + tuple(k.shape[2:]), dtype=k.dtype, device=device)
         vpool = torch.zeros((n_pages, ps) + tuple(v.shape[2:]), dtype=v.dtype, device=device)
