@@ -31,3 +31,21 @@ def test_seeded_and_bf16_valued():
         assert np.array_equal(a[n], b[n])
         bits = a[n].view(np.uint32)
         assert np.all(bits & 0xFFFF == 0)  # bf16 values held in float32
+
+
+def test_sweep_cases_are_seeded_and_well_formed():
+    for i in range(48):
+        spec, data, kvb = W.sweep_case(i)
+        again = W.sweep_case(i)[1]
+        B, Sq, Hq, D = data["q"].shape
+        _, Skv, Hkv, _ = data["k"].shape
+        assert (B, Hq, Hkv, D, Skv) == (spec.B, spec.Hq, spec.Hkv, spec.D, spec.S) and spec.n_q == Sq
+        assert Hq % Hkv == 0 and D in (128, 192) and Sq >= 1 and Skv >= 1
+        for n in data:
+            assert np.array_equal(data[n], again[n])
+        if spec.paged:
+            pt = data["page_table"]
+            assert pt.shape == (B, -(-Skv // spec.page_size))
+            assert len(np.unique(pt)) == pt.size and pt.min() >= 0  # each page holds one sequence's tokens
+        if spec.masked:
+            assert data["block_mask"].shape == (B, Hq, -(-Sq // 64), -(-Skv // kvb))
