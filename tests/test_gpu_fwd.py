@@ -27,8 +27,11 @@ def _run_small(spec, **kw):
         okw["sfs_p"] = kw["sfs_p"].cpu().numpy()
     if "lazy_rescale_log2" in kw:
         okw["tau"] = kw["lazy_rescale_log2"]
+    ukw = {}
+    if "softmax_scale" in kw:
+        okw["softmax_scale"] = ukw["softmax_scale"] = kw["softmax_scale"]
     ref = Hn.oracle_output(spec, data, ops, **okw)
-    unq = Hn.unquantized_output(spec, data)
+    unq = Hn.unquantized_output(spec, data, **ukw)
     return Hn.assert_parity(gpu, ref, unq, what=spec.name)
 
 
@@ -80,6 +83,15 @@ def test_sfs_p_and_tau_variants():
     _run_small(spec, sfs_p=sp)
     _run_small(spec, lazy_rescale_log2=0.0)
     _run_small(spec, lazy_rescale_log2=12.0)
+
+
+@pytest.mark.parametrize("base,D", [("tiny", 128), ("dit", 128), ("dit_i8", 128), ("gqa", 128), ("sparse", 128),
+                                    ("gqa", 192), ("dit", 192)])
+@pytest.mark.parametrize("scale", [0.01, 0.3])
+def test_softmax_scale_variants(base, D, scale):
+    # a flatter (0.01) and a sharper (0.3) softmax than 1/sqrt(D): the
+    # lazy reference moves more often and P spans more of the E4M3 range
+    _run_small(W.small_spec(base, 300, B=1, Hq=4, Hkv=2, causal=True, D=D), softmax_scale=scale)
 
 
 def test_masked_blocks_with_nan_are_never_read():
