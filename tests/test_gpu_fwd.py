@@ -77,8 +77,9 @@ def test_small_paged_page_sizes(page_size, masked):
     _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=2, masked=masked, page_size=page_size))
 
 
-def test_sfs_p_and_tau_variants():
-    spec = W.small_spec("gqa", 320, B=1, Hq=4, Hkv=2)
+@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "sparse", "tiny"])
+def test_sfs_p_and_tau_variants(base):
+    spec = W.small_spec(base, 320, B=1, Hq=4, Hkv=2)
     sp = torch.tensor([1.0, 0.25, 0.1, 2.0], dtype=torch.float32, device="cuda")
     _run_small(spec, sfs_p=sp)
     _run_small(spec, lazy_rescale_log2=0.0)
