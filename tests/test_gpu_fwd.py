@@ -135,6 +135,39 @@ def test_strided_q_and_output():
     assert torch.count_nonzero(out[:, :, 0]) == 0 and torch.count_nonzero(out[:, :, 3]) == 0
 
 
+@pytest.mark.parametrize("base", ["gqa", "dit_i8", "sparse"])
+def test_fused_qkv_codes(base):
+    # Q, K and V codes written by the quantizer into one fused [B, S, Hq + 2 Hkv,
+    # D] buffer (the layout of a fused QKV projection) and read back through
+    # head-strided views
+    import fmha_fwd_amd as F
+    spec = W.small_spec(base, 300, B=2, Hq=4, Hkv=2, causal=True, masked=False, paged=False)
+    print(f"fwd fused qkv {spec}", flush=True)
+    data = W.generate(spec)
+    Hq, Hkv = spec.Hq, spec.Hkv
+    fmts = (spec.q_fmt, spec.k_fmt, spec.v_fmt)
+    tdt = {"int8": torch.int8, "e4m3": torch.float8_e4m3fn, "bf16": torch.bfloat16}
+    # one fused buffer per code type (int8 Q/K beside an E4M3 V use two)
+    bufs = {f: torch.zeros((2, 300, Hq + 2 * Hkv, 128), dtype=tdt[f], device="cuda") for f in set(fmts)}
+    views = (bufs[fmts[0]][:, :, :Hq], bufs[fmts[1]][:, :, Hq:Hq + Hkv], bufs[fmts[2]][:, :, Hq + Hkv:])
+    t, sc = [], []
+    for name, fmt, view in zip(("q", "k", "v"), fmts, views):
+        x = Hn.to_gpu_bf16(data[name])
+        if fmt == "bf16":
+            t.append(x)
+            sc.append(None)
+        else:
+            c, s_ = F.quantize_blocks(x, fmt, codes=view)
+            assert c.data_ptr() == view.data_ptr()
+            t.append(view)
+            sc.append(s_)
+    o = F.fwd(t[0], t[1], t[2], sfs_q=sc[0], sfs_k=sc[1], sfs_v=sc[2], causal=True)
+    torch.cuda.synchronize()
+    ops = Hn.oracle_operands(spec, data)
+    Hn.assert_parity(o.float().cpu().numpy(), Hn.oracle_output(spec, data, ops), Hn.unquantized_output(spec, data),
+                     what=f"fused qkv {base}")
+
+
 def test_kv_sequence_beyond_2gib():
     # K/V token strides of 4 MiB: each sequence spans more than 2^31 bytes,
     # so every tile gets a buffer resource of its own
