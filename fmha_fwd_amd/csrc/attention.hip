@@ -663,9 +663,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     return acc;
   };
 
-  // S^T with the wave's issue priority raised while its MFMAs are issued:
-  // the other wave on the SIMD is then usually in its softmax, and the
-  // matrix core gets its next block sooner (+1.5-2 % measured).
+  // S^T with the wave's issue priority raised around the K operand reads
+  // (+1.5-2 % measured).  The compiler issues the S MFMAs themselves after
+  // the priority drop; keeping them inside the raised region measured no
+  // different.
   auto qk_raised = [&](const lds_u8* kb) {
     __builtin_amdgcn_s_setprio(1);
     const SAcc<C::MT> acc = qk(kb, std::true_type{});
