@@ -39,10 +39,20 @@ def mixed_peak(qk_fmt, pv_fmt):
     return 1.0 / (0.5 / PEAK[qk_fmt] + 0.5 / PEAK[pv_fmt])
 
 
+def code_text(path):
+    """Source text with comments and blank space removed: what a traffic
+    record's hash covers (a comment edit does not change the kernel)."""
+    import re
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", " ", txt)
+    return " ".join(txt.split()).encode()
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in ("attention.hip", "device_common.h"):
-        h.update(open(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f), "rb").read())
+        h.update(code_text(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f)))
     return h.hexdigest()[:16]
 
 
@@ -219,7 +229,7 @@ def nvfp4_bytes(M, K):
 def nvfp4_source_hash():
     h = hashlib.sha256()
     for f in ("nvfp4.hip", "device_common.h"):
-        h.update(open(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f), "rb").read())
+        h.update(code_text(os.path.join(ROOT, "fmha_fwd_amd", "csrc", f)))
     return h.hexdigest()[:16]
 
 
