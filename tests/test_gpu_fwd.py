@@ -464,6 +464,7 @@ FULL = [
     ("gqa_d192", [(0, 0), (1, 63)], "sample"),
     ("dit_d192", [(0, 0), (0, 39)], "sample"),
     ("sparse_d192", [(0, 0), (3, 31)], "sample"),
+    ("sparse_contig", [(1, 5), (2, 17)], "sample"),
 ]
 
 
