@@ -19,6 +19,8 @@ Configurations (d = 128 throughout; `small_spec` can set d = 192):
   gqa_chunk  the gqa inputs with only the last 256 query positions (a causal
              prefill chunk against 8192 keys)
   sparse_contig  the sparse inputs with K/V contiguous (the cost of paging)
+  sparse_dense   the same inputs with contiguous K/V and no mask (the dense
+                 attention the block mask thins out)
   dit_i8_d192, gqa_d192, dit_d192, sparse_d192  the dit_i8, gqa, dit and
              sparse shapes and formats at head dim 192 (own spawn keys 9, 10,
              11 and 12)
@@ -103,6 +105,8 @@ SPECS = {
     "sparse_d192": Spec("sparse_d192", 12, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True, paged=True, D=192),
     # the sparse inputs (same spawn key: same Q, K, V and mask) with K/V contiguous instead of paged
     "sparse_contig": Spec("sparse_contig", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True),
+    # ... and with no block mask at all: the dense attention the mask thins out
+    "sparse_dense": Spec("sparse_dense", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3"),
 }
 
 

@@ -465,6 +465,7 @@ FULL = [
     ("dit_d192", [(0, 0), (0, 39)], "sample"),
     ("sparse_d192", [(0, 0), (3, 31)], "sample"),
     ("sparse_contig", [(1, 5), (2, 17)], "sample"),
+    ("sparse_dense", [(0, 3), (3, 30)], "sample"),
 ]
 
 
