@@ -412,7 +412,9 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        for name, x, fmt, c, s in quant:
+        if len(quant) > 1:  # Q, K and V together: one launch
+            F.quantize_blocks_batch([(x, fmt, c, s) for _, x, fmt, c, s in quant], stream=stream)
+        for name, x, fmt, c, s in quant[:1] if len(quant) == 1 else ():
             F.quantize_blocks(x, fmt, codes=c, scales=s, stream=stream)
         kk, vv = ops["k"], ops["v"]
         if ev is not None:

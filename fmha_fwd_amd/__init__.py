@@ -18,12 +18,20 @@ LIB_PATH = os.environ.get("FMHA_LIB") or os.path.join(os.path.dirname(os.path.ab
 
 FMHA_DT_BF16, FMHA_DT_E4M3, FMHA_DT_INT8 = 1, 2, 3
 FMHA_OK, FMHA_ERR_INVALID, FMHA_ERR_UNSUPPORTED, FMHA_ERR_HIP = 0, -1, -2, -3
-EXPORTED = ("fmha_quantize_blocks", "fmha_fwd", "fmha_quantize_nvfp4", "fmha_last_error", "fmha_abi_version")
+EXPORTED = ("fmha_quantize_blocks", "fmha_quantize_blocks_batch", "fmha_fwd", "fmha_quantize_nvfp4", "fmha_last_error",
+            "fmha_abi_version")
+MAX_QUANTIZE_JOBS = 8
 
 
 class FmhaTensor(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class FmhaQuantizeJob(ctypes.Structure):
+    _fields_ = [("x", FmhaTensor), ("codes", FmhaTensor), ("scales", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32)]
 
 
 class FmhaFwdParams(ctypes.Structure):
@@ -69,6 +77,8 @@ def lib_handle():
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_void_p]
         lib.fmha_quantize_blocks.restype = ctypes.c_int
+        lib.fmha_quantize_blocks_batch.argtypes = [ctypes.POINTER(FmhaQuantizeJob), ctypes.c_int32, ctypes.c_void_p]
+        lib.fmha_quantize_blocks_batch.restype = ctypes.c_int
         lib.fmha_fwd.argtypes = [ctypes.POINTER(FmhaFwdParams), ctypes.c_void_p]
         lib.fmha_fwd.restype = ctypes.c_int
         lib.fmha_quantize_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -143,6 +153,37 @@ def quantize_blocks(x, dtype="e4m3", *, codes=None, scales=None, stream=None):
     _check(lib_handle().fmha_quantize_blocks(ctypes.byref(xt), ctypes.byref(ct), scales.data_ptr(),
                                              B, S, H, D, 64, _stream(stream)))
     return codes, scales
+
+
+def quantize_blocks_batch(jobs, *, stream=None):
+    """Several `quantize_blocks` calls in one launch.  jobs: a list of
+    (x, dtype) or (x, dtype, codes, scales) with x bf16 [B, S, H, D] (one D
+    for all).  Returns a list of (codes, scales), bit-identical to separate
+    calls."""
+    import torch
+    if len(jobs) > MAX_QUANTIZE_JOBS:
+        raise ValueError(f"at most {MAX_QUANTIZE_JOBS} jobs per launch")
+    arr = (FmhaQuantizeJob * max(1, len(jobs)))()
+    out = []
+    for i, job in enumerate(jobs):
+        x, dtype = job[0], job[1]
+        codes = job[2] if len(job) > 2 else None
+        scales = job[3] if len(job) > 3 else None
+        _require_cuda(x)
+        B, S, H, D = x.shape
+        tdt = {"int8": torch.int8, "e4m3": torch.float8_e4m3fn}[dtype]
+        if codes is None:
+            codes = torch.empty((B, S, H, D), dtype=tdt, device=x.device)
+        if scales is None:
+            scales = torch.empty((B, H, (S + 63) // 64), dtype=torch.float32, device=x.device)
+        if not scales.is_contiguous():
+            raise ValueError("scales must be contiguous")
+        if tuple(codes.shape) != (B, S, H, D) or tuple(scales.shape) != (B, H, (S + 63) // 64):
+            raise ValueError(f"job {i}: codes must be {(B, S, H, D)} and scales {(B, H, (S + 63) // 64)}")
+        arr[i] = FmhaQuantizeJob(_tensor(x), _tensor(codes), scales.data_ptr(), B, S, H, D, 64)
+        out.append((codes, scales))
+    _check(lib_handle().fmha_quantize_blocks_batch(arr, len(jobs), _stream(stream)))
+    return out
 
 
 def quantize_nvfp4(x, *, codes=None, block_scales=None, token_scales=None, stream=None):

@@ -68,44 +68,86 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-uint32_t fmha_abi_version(void) { return 0x000300u; }
+uint32_t fmha_abi_version(void) { return 0x000400u; }
 
 const char* fmha_last_error(void) { return g_last_error.c_str(); }
 
+namespace {
+
+// Validates one block quantisation (messages prefixed with `who`) and fills
+// its kernel arguments; *empty is set for a no-op (B, S or H equal to 0).
+int quant_args(const char* who, const fmha_tensor* x, const fmha_tensor* codes, float* scales, int32_t B,
+               int32_t S, int32_t H, int32_t D, int32_t block_tokens, fmha::QuantArgs* a, bool* empty) {
+  if (!x || !codes) return fail(FMHA_ERR_INVALID, "%s: null tensor descriptor", who);
+  if (B < 0 || S < 0 || H < 0) return fail(FMHA_ERR_INVALID, "%s: negative size (B=%d S=%d H=%d)", who, B, S, H);
+  if (D != 128 && D != 192) return fail(FMHA_ERR_UNSUPPORTED, "%s: D=%d (128 or 192 are supported)", who, D);
+  if (block_tokens != 64)
+    return fail(FMHA_ERR_UNSUPPORTED, "%s: block_tokens=%d (only 64 is supported)", who, block_tokens);
+  if (x->dtype != FMHA_DT_BF16) return fail(FMHA_ERR_INVALID, "%s: x must be bf16", who);
+  if (codes->dtype != FMHA_DT_INT8 && codes->dtype != FMHA_DT_E4M3)
+    return fail(FMHA_ERR_INVALID, "%s: codes must be int8 or e4m3", who);
+  *empty = (int64_t)B * S * H == 0;
+  char name[64];
+  int r;
+  snprintf(name, sizeof name, "%s x", who);
+  if ((r = check_tensor(name, *x, !*empty)) != FMHA_OK) return r;
+  snprintf(name, sizeof name, "%s codes", who);
+  if ((r = check_tensor(name, *codes, !*empty)) != FMHA_OK) return r;
+  if (*empty) return FMHA_OK;
+  if (!scales) return fail(FMHA_ERR_INVALID, "%s: null scales", who);
+  if (reinterpret_cast<uintptr_t>(scales) % 4 != 0) return fail(FMHA_ERR_INVALID, "%s: scales not 4-byte aligned", who);
+  *a = fmha::QuantArgs{};
+  a->x = static_cast<const uint8_t*>(x->ptr);
+  a->x_sb = x->stride_b * 2;
+  a->x_ss = x->stride_s * 2;
+  a->x_sh = x->stride_h * 2;
+  a->codes = static_cast<uint8_t*>(codes->ptr);
+  a->c_sb = codes->stride_b;
+  a->c_ss = codes->stride_s;
+  a->c_sh = codes->stride_h;
+  a->scales = scales;
+  a->B = B;
+  a->S = S;
+  a->H = H;
+  a->nblk = (S + 63) / 64;
+  a->D = D;
+  a->out_fmt = codes->dtype == FMHA_DT_INT8 ? fmha::FMT_INT8 : fmha::FMT_E4M3;
+  return FMHA_OK;
+}
+
+}  // namespace
+
 int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes, float* scales, int32_t B, int32_t S,
                          int32_t H, int32_t D, int32_t block_tokens, fmha_stream_t stream) {
-  if (!x || !codes) return fail(FMHA_ERR_INVALID, "quantize: null tensor descriptor");
-  if (B < 0 || S < 0 || H < 0) return fail(FMHA_ERR_INVALID, "quantize: negative size (B=%d S=%d H=%d)", B, S, H);
-  if (D != 128 && D != 192) return fail(FMHA_ERR_UNSUPPORTED, "quantize: D=%d (128 or 192 are supported)", D);
-  if (block_tokens != 64) return fail(FMHA_ERR_UNSUPPORTED, "quantize: block_tokens=%d (only 64 is supported)", block_tokens);
-  if (x->dtype != FMHA_DT_BF16) return fail(FMHA_ERR_INVALID, "quantize: x must be bf16");
-  if (codes->dtype != FMHA_DT_INT8 && codes->dtype != FMHA_DT_E4M3)
-    return fail(FMHA_ERR_INVALID, "quantize: codes must be int8 or e4m3");
-  const bool empty = (int64_t)B * S * H == 0;
-  int r;
-  if ((r = check_tensor("quantize x", *x, !empty)) != FMHA_OK) return r;
-  if ((r = check_tensor("quantize codes", *codes, !empty)) != FMHA_OK) return r;
+  fmha::QuantArgs a;
+  bool empty = false;
+  const int r = quant_args("quantize", x, codes, scales, B, S, H, D, block_tokens, &a, &empty);
+  if (r != FMHA_OK) return r;
   if (empty) return ok();
-  if (!scales) return fail(FMHA_ERR_INVALID, "quantize: null scales");
-  if (reinterpret_cast<uintptr_t>(scales) % 4 != 0) return fail(FMHA_ERR_INVALID, "quantize: scales not 4-byte aligned");
-
-  fmha::QuantArgs a{};
-  a.x = static_cast<const uint8_t*>(x->ptr);
-  a.x_sb = x->stride_b * 2;
-  a.x_ss = x->stride_s * 2;
-  a.x_sh = x->stride_h * 2;
-  a.codes = static_cast<uint8_t*>(codes->ptr);
-  a.c_sb = codes->stride_b;
-  a.c_ss = codes->stride_s;
-  a.c_sh = codes->stride_h;
-  a.scales = scales;
-  a.B = B;
-  a.S = S;
-  a.H = H;
-  a.nblk = (S + 63) / 64;
-  a.D = D;
-  a.out_fmt = codes->dtype == FMHA_DT_INT8 ? fmha::FMT_INT8 : fmha::FMT_E4M3;
   return hip_status(fmha::launch_quantize_blocks(a, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+int fmha_quantize_blocks_batch(const fmha_quantize_job* jobs, int32_t n_jobs, fmha_stream_t stream) {
+  if (n_jobs < 0 || n_jobs > FMHA_MAX_QUANTIZE_JOBS)
+    return fail(FMHA_ERR_INVALID, "quantize batch: n_jobs=%d (0 to %d)", n_jobs, FMHA_MAX_QUANTIZE_JOBS);
+  if (n_jobs == 0) return ok();
+  if (!jobs) return fail(FMHA_ERR_INVALID, "quantize batch: null jobs");
+  fmha::QuantArgs a[FMHA_MAX_QUANTIZE_JOBS];
+  int n = 0;
+  for (int j = 0; j < n_jobs; ++j) {
+    const fmha_quantize_job& q = jobs[j];
+    char who[32];
+    snprintf(who, sizeof who, "quantize job %d", j);
+    bool empty = false;
+    const int r = quant_args(who, &q.x, &q.codes, q.scales, q.B, q.S, q.H, q.D, q.block_tokens, &a[n], &empty);
+    if (r != FMHA_OK) return r;
+    if (q.D != jobs[0].D)
+      return fail(FMHA_ERR_UNSUPPORTED, "quantize batch: job %d has D=%d, job 0 D=%d (one head dim per batch)", j,
+                  q.D, jobs[0].D);
+    if (!empty) ++n;
+  }
+  if (n == 0) return ok();
+  return hip_status(fmha::launch_quantize_blocks_batch(a, n, static_cast<hipStream_t>(stream)), "quantize batch launch");
 }
 
 int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t K, uint8_t* codes,

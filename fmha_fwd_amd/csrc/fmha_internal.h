@@ -22,6 +22,15 @@ struct QuantArgs {
 
 hipError_t launch_quantize_blocks(const QuantArgs& a, hipStream_t stream);
 
+// Up to kMaxQuantJobs quantisations of one head dim in a single launch.
+constexpr int kMaxQuantJobs = 8;
+struct QuantBatch {
+  QuantArgs job[kMaxQuantJobs];
+  int64_t first[kMaxQuantJobs + 1];  // first grid block (wave) of each job; first[n] = total
+  int n;
+};
+hipError_t launch_quantize_blocks_batch(const QuantArgs* jobs, int n, hipStream_t stream);
+
 struct Nvfp4Args {
   const uint8_t* x; int64_t x_rs;   // bf16 [M, K], row stride in bytes
   uint8_t* codes; int64_t c_rs;     // [M, K/2], two E2M1 codes per byte

@@ -48,12 +48,8 @@ __device__ __forceinline__ uint2 encode8(const uint4& v, float inv) {
 // 64 x 192 blocks: chunk c = lane + 64 i of the block is token c / 24,
 // channels 8 (c % 24) .. +8.
 template <int OUT>
-__global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel_d192(QuantArgs a) {
+__device__ __forceinline__ void quantize_block_d192(const QuantArgs& a, const int64_t unit, const int lane) {
   constexpr int CPR = 24, PER_LANE = CPR;  // 64 rows x 24 chunks over 64 lanes
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t total = (int64_t)a.B * a.H * a.nblk;
-  if (unit >= total) return;  // uniform per wave
   const int blk = (int)(unit % a.nblk);
   const int64_t bh = unit / a.nblk;
   const int h = (int)(bh % a.H);
@@ -100,12 +96,15 @@ __global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel_d192(Quant
   if (lane == 0) a.scales[bh * a.nblk + blk] = scale;
 }
 
-template <int OUT>  // FMT_INT8 or FMT_E4M3
-__global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel(QuantArgs a) {
-  const int lane = threadIdx.x & 63;
+template <int OUT>
+__global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel_d192(QuantArgs a) {
   const int64_t unit = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t total = (int64_t)a.B * a.H * a.nblk;
-  if (unit >= total) return;  // uniform per wave
+  if (unit >= (int64_t)a.B * a.H * a.nblk) return;  // uniform per wave
+  quantize_block_d192<OUT>(a, unit, threadIdx.x & 63);
+}
+
+template <int OUT>  // FMT_INT8 or FMT_E4M3
+__device__ __forceinline__ void quantize_block_d128(const QuantArgs& a, const int64_t unit, const int lane) {
   const int blk = (int)(unit % a.nblk);
   const int64_t bh = unit / a.nblk;
   const int h = (int)(bh % a.H);
@@ -156,7 +155,55 @@ __global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel(QuantArgs 
   if (lane == 0) a.scales[bh * a.nblk + blk] = scale;
 }
 
+template <int OUT>
+__global__ __launch_bounds__(kWaves * 64) void quantize_blocks_kernel(QuantArgs a) {
+  const int64_t unit = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (unit >= (int64_t)a.B * a.H * a.nblk) return;  // uniform per wave
+  quantize_block_d128<OUT>(a, unit, threadIdx.x & 63);
+}
+
+// Several tensors of one head dim in one launch: wave w of the grid takes
+// block w - first[j] of job j, first[j] <= w < first[j + 1] (the blocks of
+// each job in the order of a single launch).
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void quantize_blocks_batch_kernel(QuantBatch jb) {
+  const int64_t unit = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (unit >= jb.first[jb.n]) return;  // uniform per wave
+  int j = 0;
+  while (unit >= jb.first[j + 1]) ++j;
+  const QuantArgs& a = jb.job[j];
+  const int lane = threadIdx.x & 63;
+  if constexpr (D == 192) {
+    if (a.out_fmt == FMT_INT8) quantize_block_d192<FMT_INT8>(a, unit - jb.first[j], lane);
+    else quantize_block_d192<FMT_E4M3>(a, unit - jb.first[j], lane);
+  } else {
+    if (a.out_fmt == FMT_INT8) quantize_block_d128<FMT_INT8>(a, unit - jb.first[j], lane);
+    else quantize_block_d128<FMT_E4M3>(a, unit - jb.first[j], lane);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_blocks_batch(const QuantArgs* jobs, int n, hipStream_t stream) {
+  if (n < 1 || n > kMaxQuantJobs) return hipErrorInvalidValue;
+  QuantBatch jb{};
+  jb.n = n;
+  jb.first[0] = 0;
+  for (int j = 0; j < n; ++j) {
+    if (jobs[j].D != jobs[0].D) return hipErrorInvalidValue;
+    jb.job[j] = jobs[j];
+    jb.first[j + 1] = jb.first[j] + (int64_t)jobs[j].B * jobs[j].H * jobs[j].nblk;
+  }
+  const int64_t units = jb.first[n];
+  if (units == 0) return hipSuccess;
+  const int64_t grid = (units + kWaves - 1) / kWaves;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (jobs[0].D == 192)
+    hipLaunchKernelGGL(quantize_blocks_batch_kernel<192>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, jb);
+  else
+    hipLaunchKernelGGL(quantize_blocks_batch_kernel<128>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, jb);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_blocks(const QuantArgs& a, hipStream_t stream) {
   const int64_t units = (int64_t)a.B * a.H * a.nblk;

@@ -6,7 +6,8 @@
  *   fmha_quantize_blocks  per-(batch, head, 64-token block) quantisation of a
  *                         bf16 tensor to int8 or E4M3 codes plus one fp32
  *                         scale per block (SageAttention-style block scale
- *                         factors).
+ *                         factors); fmha_quantize_blocks_batch does several
+ *                         in one launch.
  *   fmha_fwd              fused attention forward over int8 / E4M3 / bf16
  *                         Q, K, V with per-block scale factors, online softmax
  *                         with lazy rescaling, P requantised to the V format,
@@ -110,6 +111,30 @@ typedef void* fmha_stream_t;
 int fmha_quantize_blocks(const fmha_tensor* x, const fmha_tensor* codes,
                          float* scales, int32_t B, int32_t S, int32_t H,
                          int32_t D, int32_t block_tokens, fmha_stream_t stream);
+
+/*
+ * fmha_quantize_blocks_batch -- up to FMHA_MAX_QUANTIZE_JOBS block
+ * quantisations in one launch (the Q, K and V of one attention call: the
+ * #2711 page quantises all three with their own scale factors, 코드 분석 2).
+ * Each job is exactly one fmha_quantize_blocks call (same arguments, same
+ * results bit for bit); jobs may mix int8 and E4M3 codes and shapes, but not
+ * head dims (every job's D must equal job 0's, else FMHA_ERR_UNSUPPORTED).
+ * No job's codes or scales may overlap another job's input or output.
+ * Every job is validated before any HIP call; an error names the job.
+ * n_jobs == 0 is a no-op; n_jobs outside [0, FMHA_MAX_QUANTIZE_JOBS] is
+ * FMHA_ERR_INVALID.
+ */
+#define FMHA_MAX_QUANTIZE_JOBS 8
+typedef struct {
+  fmha_tensor x;          /* bf16 [B, S, H, D]; read only */
+  fmha_tensor codes;      /* int8 or E4M3 [B, S, H, D]; written */
+  float* scales;          /* fp32 [B, H, ceil(S / block_tokens)], contiguous */
+  int32_t B, S, H, D;
+  int32_t block_tokens;   /* 64 */
+} fmha_quantize_job;
+
+int fmha_quantize_blocks_batch(const fmha_quantize_job* jobs, int32_t n_jobs,
+                               fmha_stream_t stream);
 
 /*
  * Parameters of fmha_fwd.  Zero-initialise, then set struct_size =
@@ -234,7 +259,8 @@ int fmha_quantize_nvfp4(const void* x, int64_t x_row_stride, int32_t M, int32_t 
  * valid until the next fmha_* call on that thread. */
 const char* fmha_last_error(void);
 
-/* ABI version: 0xMMmmpp (0x000300: fmha_quantize_nvfp4 added). */
+/* ABI version: 0xMMmmpp (0x000300: fmha_quantize_nvfp4 added; 0x000400:
+ * fmha_quantize_blocks_batch added). */
 uint32_t fmha_abi_version(void);
 
 #ifdef __cplusplus

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in syms, name
         assert getattr(lib, name) is not None
-    assert lib.fmha_abi_version() == 0x000300
+    assert lib.fmha_abi_version() == 0x000400
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -178,6 +178,53 @@ def test_quantize_rejects_bad_arguments(lib, kw, code, msg):
 def test_quantize_empty_is_a_no_op(lib):
     x, c = _tensor(F.FMHA_DT_BF16), _tensor(F.FMHA_DT_INT8)
     assert lib.fmha_quantize_blocks(ctypes.byref(x), ctypes.byref(c), None, 0, 64, 4, 128, 64, None) == F.FMHA_OK
+
+
+def _job(B=1, S=64, H=4, D=128, block=64, xdt=F.FMHA_DT_BF16, cdt=F.FMHA_DT_E4M3, xptr=FAKE, scales=FAKE):
+    return F.FmhaQuantizeJob(_tensor(xdt, ptr=xptr), _tensor(cdt), scales, B, S, H, D, block)
+
+
+def _batch(lib, jobs, n=None):
+    arr = (F.FmhaQuantizeJob * max(1, len(jobs)))(*jobs)
+    rc = lib.fmha_quantize_blocks_batch(arr, len(jobs) if n is None else n, None)
+    return rc, lib.fmha_last_error().decode()
+
+
+@pytest.mark.parametrize("jobs,n,code,msg", [
+    ([_job()], -1, F.FMHA_ERR_INVALID, "n_jobs=-1"),
+    ([_job()] * 9, None, F.FMHA_ERR_INVALID, "n_jobs=9"),
+    ([_job(), _job(D=64)], None, F.FMHA_ERR_UNSUPPORTED, "quantize job 1: D=64"),
+    ([_job(), _job(D=192)], None, F.FMHA_ERR_UNSUPPORTED, "one head dim per batch"),
+    ([_job(), _job(), _job(xptr=0)], None, F.FMHA_ERR_INVALID, "quantize job 2 x: null pointer"),
+    ([_job(cdt=F.FMHA_DT_BF16)], None, F.FMHA_ERR_INVALID, "quantize job 0: codes must be int8 or e4m3"),
+    ([_job(), _job(scales=0)], None, F.FMHA_ERR_INVALID, "quantize job 1: null scales"),
+    ([_job(block=32)], None, F.FMHA_ERR_UNSUPPORTED, "block_tokens"),
+])
+def test_quantize_batch_rejects_bad_arguments(lib, jobs, n, code, msg):
+    rc, err = _batch(lib, jobs, n)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_quantize_batch_empty_is_a_no_op(lib):
+    assert _batch(lib, [], 0) == (F.FMHA_OK, "")
+    assert lib.fmha_quantize_blocks_batch(None, 0, None) == F.FMHA_OK
+    rc, err = _batch(lib, [_job(B=0), _job(H=0)])
+    assert rc == F.FMHA_OK and err == ""
+
+
+def test_quantize_job_layout_matches_header(tmp_path):
+    fields = [f for f, _ in F.FmhaQuantizeJob._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
+           'printf("%zu %d\\n", sizeof(fmha_quantize_job), FMHA_MAX_QUANTIZE_JOBS);']
+    src += [f'printf("%zu\\n", offsetof(fmha_quantize_job, {f}));' for f in fields]
+    src.append("return 0;}")
+    c = tmp_path / "job.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "job"
+    subprocess.run(["gcc", str(c), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(F.FmhaQuantizeJob) and vals[1] == F.MAX_QUANTIZE_JOBS
+    assert vals[2:] == [getattr(F.FmhaQuantizeJob, f).offset for f in fields]
 
 
 def _nvfp4(lib, **kw):

@@ -128,3 +128,45 @@ def test_dead_blocks_with_negative_zeros_and_subnormals(fmt, d):
     _check(x, fmt, c, s)
     assert not c.view(np.uint8).any(), "dead blocks must hold code 0x00 only"
     assert (s == 1.0).all()
+
+
+@pytest.mark.parametrize("D", [128, 192])
+def test_batch_matches_single_calls_and_oracle(D):
+    # one launch for up to eight tensors of mixed formats and shapes (a GQA
+    # Q / K / V set, a head-strided view, ragged tails, a dead block with
+    # negative zeros): bit-identical to one call per tensor and to the oracle
+    import fmha_fwd_amd as F
+    rng = np.random.default_rng(31 + D)
+    shapes = [(1, 300, 8, D), (1, 1000, 2, D), (1, 1000, 2, D), (2, 65, 3, D), (1, 1, 1, D), (3, 129, 2, D),
+              (1, 64, 4, D), (2, 200, 1, D)]
+    fmts = ["int8", "int8", "e4m3", "e4m3", "int8", "e4m3", "e4m3", "int8"]
+    xs = []
+    for i, sh in enumerate(shapes):
+        x = rng.standard_normal(sh).astype(np.float32) * np.float32(np.exp(rng.uniform(-4, 4)))
+        if i == 3:
+            x[0, 0:64, 1] = -0.0  # a dead block of negative zeros
+        xs.append(_bf16(x))
+    gx = [torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda() for x in xs]
+    big = torch.zeros((1, 1000, 5, D), dtype=torch.bfloat16, device="cuda")  # job 1 read through a strided view
+    big[:, :, 3:5] = gx[1]
+    gx[1] = big[:, :, 3:5]
+    print(f"quantize batch D={D}: {len(shapes)} jobs", flush=True)
+    out = F.quantize_blocks_batch([(x, f) for x, f in zip(gx, fmts)])
+    single = [F.quantize_blocks(x, f) for x, f in zip(gx, fmts)]
+    torch.cuda.synchronize()
+    for i, ((c, s), (c1, s1), x, f) in enumerate(zip(out, single, xs, fmts)):
+        assert torch.equal(c.view(torch.uint8), c1.view(torch.uint8)), f"job {i}: codes differ from a single call"
+        assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), f"job {i}: scales differ from a single call"
+        _check(x, f, c.view(torch.int8 if f == "int8" else torch.uint8).cpu().numpy(), s.cpu().numpy())
+
+
+def test_batch_of_one_and_empty_jobs():
+    import fmha_fwd_amd as F
+    x = torch.randn((1, 130, 2, 128)).to(torch.bfloat16).cuda()
+    e = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    (c, s), (ce, se) = F.quantize_blocks_batch([(x, "e4m3"), (e, "int8")])
+    c1, s1 = F.quantize_blocks(x, "e4m3")
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.uint8), c1.view(torch.uint8)) and torch.equal(s, s1)
+    assert ce.numel() == 0 and se.numel() == 0
+    assert F.quantize_blocks_batch([]) == []
