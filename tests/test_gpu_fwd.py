@@ -354,6 +354,14 @@ def test_rows_of_several_heads_per_wave(base, hq, sq, causal):
     _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=causal, sq=sq, masked=False))
 
 
+@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "tiny", "sparse"])
+@pytest.mark.parametrize("hq,sq", [(16, 1), (16, 5), (32, 3)])
+def test_short_query_ranges_at_head_dim_192(base, hq, sq):
+    # at d = 192 short query ranges of large groups fall back to whole-wave
+    # head packing (no heads inside a wave)
+    _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=True, sq=sq, masked=False, D=192))
+
+
 @pytest.mark.parametrize("base", ["gqa", "dit_i8", "sparse"])
 @pytest.mark.parametrize("sq", [1, 7, 16])
 @pytest.mark.parametrize("causal", [False, True])
