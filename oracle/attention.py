@@ -50,7 +50,11 @@ fused or integer accumulation is only more accurate), then rounds at most
 four more times in forming the exponent s2 - m - log2(sp) (the scale
 product, the running maximum, the log of sp and the fused multiply-add: at
 most 4 u (|s2| + |m| + |log2 sp|)), and evaluates 2^x to within 2 ulp
-(2^-22 relative).  The relative error of P is then at most ln 2 times the
+(2^-22 relative).  The reference maximum m is itself the binary32 score of
+some key of the sub-tile that set it, so its accumulation error enters the
+exponent too: at most the largest gamma_D * sum_d |q_d k_d| among the keys
+whose score plus that bound reaches the sub-tile's maximum (the only keys
+that can come out on top).  The relative error of P is then at most ln 2 times the
 exponent error plus 2^-22, to first order.
 """
 import math
@@ -63,15 +67,33 @@ LOG2E = 1.0 / math.log(2.0)
 U32 = 2.0 ** -24  # unit roundoff of IEEE binary32
 
 
-def binary32_p_error(q, k, s, m, D, c, sp):
+def binary32_accumulation_error(q, k, D, c):
+    """Bound on the error of a binary32 score c * (q . k), log2 units, for
+    every pair of rows of q and k: c * gamma_D * sum_d |q_d k_d|."""
+    gamma = D * U32 / (1.0 - D * U32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return c * gamma * (np.abs(q) @ np.abs(k).T)
+
+
+def _max_error(s, err, t):
+    """Error bound of a binary32 maximum of the scores s (rows; -inf where
+    invalid) whose exact maximum is t: a key can come out on top only if its
+    score plus its error reaches t, so the largest error among those keys
+    bounds the computed maximum's distance from t."""
+    with np.errstate(invalid="ignore"):
+        cand = np.isfinite(s) & (s + err >= t[:, None])
+    return np.where(cand, err, 0.0).max(axis=1) if s.shape[1] else np.zeros(s.shape[0])
+
+
+def binary32_p_error(q, k, s, m, D, c, sp, m_err=0.0):
     """Relative error bound of P = 2^(s - m) / sp for a binary32 kernel (see
     the module docstring): s = c * (q . k) are the fp64 log2-domain scores of
-    the pairs (rows of q against rows of k), m the row's reference maximum."""
-    gamma = D * U32 / (1.0 - D * U32)
-    acc = c * gamma * (np.abs(q) @ np.abs(k).T)
+    the pairs (rows of q against rows of k), m the row's reference maximum and
+    m_err (per row) the accumulation error bound of the score that set it."""
+    acc = binary32_accumulation_error(q, k, D, c)
     with np.errstate(invalid="ignore"):
         rnd = 4.0 * U32 * (np.abs(s) + np.abs(m)[:, None] + abs(math.log2(sp)))
-    return math.log(2.0) * (acc + rnd) + 2.0 ** -22
+    return math.log(2.0) * (acc + np.asarray(m_err, dtype=np.float64).reshape(-1, 1) + rnd) + 2.0 ** -22
 
 
 def dequantize(codes, fmt, scales=None, block_tokens=64):
@@ -148,8 +170,15 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
     valid = valid_pairs(rows, Sq, Skv, causal, mask_rows)
     with np.errstate(invalid="ignore", over="ignore"):
         s2 = (q @ k.T) * (softmax_scale * LOG2E)
+    b32 = isinstance(flip_eps, str)
+    if b32:
+        assert flip_eps == "binary32", flip_eps
+        acc_err = np.where(valid, binary32_accumulation_error(q, k, D, softmax_scale * LOG2E), 0.0)
+    m_err = np.zeros(n)  # accumulation error bound of the score that set m (binary32 model)
     if mode == "exact":
         m = np.where(valid, s2, -np.inf).max(axis=1) if Skv else np.full(n, -np.inf)
+        if b32 and Skv:
+            m_err = _max_error(np.where(valid, s2, -np.inf), acc_err, m)
     else:
         m = np.full(n, -np.inf)
     num = np.zeros((n, D))
@@ -171,6 +200,8 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
             num[trig] *= alpha[trig, None]
             den[trig] *= alpha[trig]
             m = np.where(trig, t, m)
+            if b32:
+                m_err = np.where(trig, _max_error(s, acc_err[:, cols], t), m_err)
         with np.errstate(invalid="ignore", over="ignore"):
             p = np.where(vs, np.exp2(s - m[:, None]), 0.0)
         w = _quantize_p(p / sp, p_format) * sp
@@ -182,10 +213,9 @@ def attention_head(q, k, v, rows, *, Sq, softmax_scale, causal=False,
         den += w.sum(axis=1)
         if flip_eps is not None:
             eps = flip_eps
-            if isinstance(flip_eps, str):
-                assert flip_eps == "binary32", flip_eps
+            if b32:
                 eps = np.where(vs, binary32_p_error(q, k[cols], np.where(vs, s, 0.0), m, D,
-                                                    softmax_scale * LOG2E, sp), 0.0)
+                                                    softmax_scale * LOG2E, sp, m_err), 0.0)
             gap = np.where(vs, rounding_gap(p / sp, p_format, eps) * sp, 0.0)
             if gap.any():
                 ties.append((cols, gap, m.copy(), vv))

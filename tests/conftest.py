@@ -52,5 +52,6 @@ def pytest_terminal_summary(terminalreporter):
             f"{ties} excused by the P-rounding bound (fraction {ties / max(n, 1):.2e})")
     worst = sorted(harness.RECORDS, key=lambda wr: -wr[1]["n_tie"] / max(wr[1]["n"], 1))[:8]
     for what, r in worst:
-        tw.line(f"  {what}: n={r['n']} n_tie={r['n_tie']} (cap {r['tie_cap']}) n_ulp={r['n_ulp']} "
+        tw.line(f"  {what}: n={r['n']} n_tie={r['n_tie']} (cap {r['tie_cap']}, oracle candidates {r['n_cand']}) "
+                f"n_ulp={r['n_ulp']} "
                 f"maxabs={r['maxabs']:.3e} cos={r['cos']:.7f}")

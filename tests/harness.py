@@ -17,8 +17,10 @@ TOL_COS_U = 0.99
 FLIP_EPS = "binary32"
 # Elements over the max-abs bar that the P-rounding bound excuses: at most
 # five in ten thousand of those compared (measured up to 2.8e-4 on the E4M3
-# Q/K inputs with per-head deviations up to 2, none elsewhere), or one row's
-# worth in small cases.
+# Q/K inputs with per-head deviations up to 2 at the default softmax scale),
+# or one row's worth in small cases, or as many as the oracle finds able to
+# cross the bar on a tie (elements whose bound exceeds it: a sharper softmax
+# concentrates a row on a few keys whose flipped P code moves the whole row).
 TIE_FRACTION = 5e-4
 TIE_FLOOR = 128
 # every parity comparison of the session, printed by the terminal summary
@@ -54,7 +56,7 @@ def oracle_operands(spec, data, heads_q=None, heads_kv=None):
 def oracle_output(spec, data, operands, rows=None, heads=None, quantized=True, **kw):
     """(O, rounding-sensitivity bound) of the quantisation-emulating oracle."""
     qd, kd, vd = operands
-    p_fmt = spec.v_fmt if quantized else None
+    p_fmt = spec.p_fmt if quantized else None
     return attention(qd, kd, vd, causal=spec.causal, block_mask=data.get("block_mask"), mode="lazy",
                      p_format=p_fmt, rows=rows, heads=heads, flip_eps=FLIP_EPS, **kw)
 
@@ -111,6 +113,16 @@ def gpu_run(spec, data, device="cuda", **fwd_kw):
 
 
 # ------------------------------------------------------------------ comparison
+def bad_mask(gpu, ref, bound):
+    """Elements that fail the max-abs bar (the n_bad of `compare`)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref_bf = bf16_round64(np.asarray(ref, dtype=np.float64))
+    diff = np.abs(gpu - ref_bf)
+    _, e = np.frexp(np.maximum(np.abs(gpu), np.abs(ref_bf)))
+    one_ulp = (diff > 0) & (diff <= np.ldexp(1.0, e - 8))
+    return (diff > TOL_MAXABS) & ~one_ulp & (diff > TOL_MAXABS + np.asarray(bound, dtype=np.float64))
+
+
 def compare(gpu, ref, bound=None):
     """Max-abs error against the oracle rounded to bf16 (differences of one
     bf16 unit in the last place are counted apart, and so are differences
@@ -128,7 +140,7 @@ def compare(gpu, ref, bound=None):
     bad = over & (diff > TOL_MAXABS + bound)
     cos = cosine(gpu, ref)
     return dict(maxabs=float(diff.max()) if diff.size else 0.0, n_bad=int(bad.sum()), n_ulp=int(one_ulp.sum()),
-                n_tie=int((over & ~bad).sum()), cos=cos, n=int(diff.size))
+                n_tie=int((over & ~bad).sum()), n_cand=int((bound > TOL_MAXABS).sum()), cos=cos, n=int(diff.size))
 
 
 def cosine(a, b):
@@ -144,10 +156,14 @@ def assert_parity(gpu, ref_and_bound, unq=None, what=""):
     method's own."""
     ref, bound = ref_and_bound
     r = compare(gpu, ref, bound)
-    r["tie_cap"] = int(max(TIE_FLOOR, TIE_FRACTION * r["n"]))
+    r["tie_cap"] = int(max(TIE_FLOOR, TIE_FRACTION * r["n"], r["n_cand"]))
     RECORDS.append((what, r))
     msg = f"{what}: {r}"
     assert np.all(np.isfinite(gpu)), msg
+    if r["n_bad"]:
+        idx = [tuple(int(x) for x in i) for i in np.argwhere(bad_mask(gpu, ref, bound))[:5]]
+        msg += " failing (index, gpu, oracle, bound): " + str([(i, float(np.asarray(gpu)[i]), float(ref[i]),
+                                                                 float(np.asarray(bound)[i])) for i in idx])
     assert r["n_bad"] == 0, msg
     assert r["n_tie"] <= r["tie_cap"], msg
     assert r["cos"] >= TOL_COS_Q, msg

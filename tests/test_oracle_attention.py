@@ -309,7 +309,7 @@ def test_binary32_bound_covers_a_binary32_evaluation(p_format):
     scale, maximum, subtraction and exp2 in float32, then the same P format).
     Every output element lies within the bound of the fp64 result, the bound
     is needed (some P values do round the other way), and it is tighter than a
-    fixed relative distance of 2^-12."""
+    fixed relative distance of 2^-11."""
     from oracle.codecs import bf16_round64, e4m3_round
     rng = np.random.default_rng(77)
     n, Skv, D = 256, 4096, 128
@@ -330,8 +330,63 @@ def test_binary32_bound_covers_a_binary32_evaluation(p_format):
     flips = int((w != w64).sum())  # P values the binary32 evaluation rounds the other way
     assert flips > 0, "no P rounded the other way: the case does not exercise the bound"
     assert np.all(np.abs(o32 - o[0, :, 0]) <= bound[0, :, 0] + 1e-9)
-    _, fixed = attention(q, k, v, mode="exact", p_format=p_format, flip_eps=2.0 ** -12)
+    _, fixed = attention(q, k, v, mode="exact", p_format=p_format, flip_eps=2.0 ** -11)
     assert bound.sum() < fixed.sum()
+
+
+def test_binary32_bound_covers_the_reference_maximum_error():
+    """Lazy attention with every score moved to the edge of its binary32
+    accumulation bound (e = c gamma_D sum_d |q_d k_d|, which some summation
+    order can reach): the key holding a sub-tile's maximum moves up, every
+    other key down, so each P = 2^(s - m) errs by ln 2 (e_j + e_m).  The
+    output stays within the oracle's bound, and some of the P values that
+    round the other way lie outside the window of the pair's own error: the
+    reference maximum's accumulation error is what covers them."""
+    from oracle.attention import LOG2E, binary32_accumulation_error, binary32_p_error
+    from oracle.codecs import e4m3_round, rounding_gap
+    rng = np.random.default_rng(5)
+    n, Skv, D, tau = 128, 2048, 128, 8.0
+    q = W_bf16(rng.standard_normal((1, n, 1, D)) * 1.5)
+    k = W_bf16(rng.standard_normal((1, Skv, 1, D)) * 1.5)
+    v = W_bf16(rng.standard_normal((1, Skv, 1, D)))
+    c = (1.0 / math.sqrt(D)) * LOG2E
+    o, bound = attention(q, k, v, mode="lazy", p_format="e4m3", tau=tau, flip_eps="binary32")
+    qq, kk, vv = q[0, :, 0], k[0, :, 0], v[0, :, 0]
+    s = (qq @ kk.T) * c
+    e = binary32_accumulation_error(qq, kk, D, c)
+    rows = np.arange(n)
+    m = np.full(n, -np.inf)       # reference from the moved scores
+    m_x = np.full(n, -np.inf)     # reference from the exact scores
+    num, den = np.zeros((n, D)), np.zeros(n)
+    flips = beyond_pair = 0
+    for t0 in range(0, Skv, 64):
+        cols = slice(t0, t0 + 64)
+        sx = s[:, cols]
+        top = np.argmax(sx, axis=1)
+        se = sx - e[:, cols]
+        se[rows, top] = sx[rows, top] + e[rows, t0 + top]
+        tx, te = sx.max(axis=1), se.max(axis=1)
+        trig = (m_x == -np.inf) | (tx - m_x > tau)
+        assert np.array_equal(trig, (m == -np.inf) | (te - m > tau))  # margins far above e
+        # rescale by the exact references' factor: the bound covers P values
+        # that round the other way; the continuous error of the factor itself
+        # is left to the max-abs bar
+        alpha = np.where(m_x == -np.inf, 0.0, np.exp2(np.where(trig, m_x - tx, 0.0)))
+        num *= alpha[:, None]
+        den *= alpha
+        m, m_x = np.where(trig, te, m), np.where(trig, tx, m_x)
+        w = e4m3_round(np.exp2(se - m[:, None]))
+        px = np.exp2(sx - m_x[:, None])
+        num += w @ vv[cols]
+        den += w.sum(axis=1)
+        flip = w != e4m3_round(px)
+        pair_only = binary32_p_error(qq, kk[cols], sx, m_x, D, c, 1.0)
+        flips += int(flip.sum())
+        beyond_pair += int((flip & (rounding_gap(px, "e4m3", pair_only) == 0)).sum())
+    o_edge = num / den[:, None]
+    assert flips > 0 and beyond_pair > 0, (flips, beyond_pair)
+    # the bound is first order: 1 % covers the products of the flips
+    assert np.all(np.abs(o_edge - o[0, :, 0]) <= 1.01 * bound[0, :, 0] + 1e-12)
 
 
 def W_bf16(x):
