@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # Published dense peaks of MI355X (TFLOP/s) and HBM bandwidth (GB/s).
-PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "int8": 5000.0}
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "e4m3": 5000.0, "int8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 METRIC = "fmha_fwd TFLOP/s (4·B·H·Sq·Skv·d, mask-aware) + % of MI355X dtype MFMA peak"
 
@@ -127,7 +127,7 @@ def cpu_baseline(spec, data, budget_s=12.0, n_heads=6):
         del todo[:64]
         bm = None if bm_all is None else bm_all[b:b + 1, [h]]
         t0 = time.perf_counter()
-        attention(*ops, causal=spec.causal, block_mask=bm, mode="lazy", p_format=spec.v_fmt, rows=rows,
+        attention(*ops, causal=spec.causal, block_mask=bm, mode="lazy", p_format=spec.p_fmt, rows=rows,
                   heads=[(0, 0)])
         t_att += time.perf_counter() - t0
         rows_done += len(rows)
@@ -144,7 +144,7 @@ def cpu_baseline(spec, data, budget_s=12.0, n_heads=6):
             "extrapolated_full_s": 4.0 * spec.D * (pair_count(spec, data) or 0) / (flops / t_att),
             "rows_total": spec.B * spec.Hq * nq,
             "sample": f"{rows_done} query rows of {len(heads)} (batch, head) pairs {heads} (each head's first, last "
-                      f"and tail-block rows, then random rows), all their valid keys, lazy {spec.v_fmt}-P oracle "
+                      f"and tail-block rows, then random rows), all their valid keys, lazy {spec.p_fmt}-P oracle "
                       f"in fp64 numpy; operand dequantisation ({t_prep:.1f} s) not counted; {t_att:.1f} s of CPU "
                       f"time",
             "seconds": round(t_att, 2)}
@@ -443,7 +443,7 @@ def main():
     pairs = pair_count(spec, data)
     flops = 4.0 * spec.D * pairs
     qk_fmt = "bf16" if spec.q_fmt == "bf16" or spec.k_fmt == "bf16" else spec.q_fmt
-    pv_fmt = spec.v_fmt
+    pv_fmt = spec.pv_mfma
     peak = mixed_peak(qk_fmt, pv_fmt)
     achieved = flops / (fwd_ms * 1e-3) / 1e12
     quant_bytes = sum(x.numel() * 3 + s.numel() * 4 for _, x, _, _, s in quant)
@@ -477,7 +477,7 @@ def main():
         "dtype": f"{qk_fmt}-qk/{pv_fmt}-pv",
         "data": "synthetic",
         "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "Sq": spec.n_q, "Skv": spec.S,
-                   "d": spec.D, "q": spec.q_fmt, "k": spec.k_fmt, "v": spec.v_fmt, "p": spec.v_fmt,
+                   "d": spec.D, "q": spec.q_fmt, "k": spec.k_fmt, "v": spec.v_fmt, "p": spec.p_fmt,
                    "causal": spec.causal, "block_sparse": spec.masked, "paged": spec.paged,
                    "unmasked_pairs": pairs, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

@@ -258,7 +258,8 @@ def fwd(q, k, v, *, sfs_q=None, sfs_k=None, sfs_v=None, sfs_p=None, causal=False
     out_dtype is "e4m3" or `out` is float8_e4m3fn; sfs_o: fp32 [Hq] output
     scale of an E4M3 o, o = encode(O / sfs_o)).
 
-    q: [B, Sq, Hq, D] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, D],
+    q: [B, Sq, Hq, D] bf16 / int8 / float8_e4m3fn.  k, v: [B, Skv, Hkv, D]
+    (v also int8 under an E4M3 Q and K, with its block scales),
     or with page_table (int32 [B, pages]) pools [num_pages, page_size, Hkv, D]
     and seq_len_kv giving Skv.  D = 128 or 192 (at 192 a bf16 Q and K with
     an E4M3 V need its scale).  sfs_*: fp32 [B, H, ceil(S/64)] block

@@ -198,7 +198,6 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
     return fail(FMHA_ERR_UNSUPPORTED, "fwd: o must be bf16 or e4m3");
   if (sfs_o && p->o.dtype != FMHA_DT_E4M3) return fail(FMHA_ERR_INVALID, "fwd: sfs_o given for a bf16 o");
   if (sfs_o && reinterpret_cast<uintptr_t>(sfs_o) % 4) return fail(FMHA_ERR_INVALID, "fwd: sfs_o misaligned");
-  if (p->v.dtype == FMHA_DT_INT8) return fail(FMHA_ERR_UNSUPPORTED, "fwd: int8 V is not supported");
   const bool empty = (int64_t)p->B * p->Sq == 0;
   const bool paged = p->page_table != nullptr;
   const bool need_kv = !empty && p->Skv > 0;
@@ -263,8 +262,8 @@ int fmha_fwd(const fmha_fwd_params* p, fmha_stream_t stream) {
     return fail(FMHA_ERR_UNSUPPORTED,
                 "fwd: no kernel for (q, k, v) = (%d, %d, %d) with scales (q %d, k %d, v %d); supported: "
                 "bf16/bf16/bf16 unscaled, int8/int8/e4m3 [q,k,v], bf16/bf16/e4m3 [v or none], "
-                "e4m3/e4m3/e4m3 [q,k,v], bf16/e4m3/e4m3 [k,v]; with D=192 the same except bf16/bf16/e4m3 "
-                "without a V scale",
+                "e4m3/e4m3/e4m3 [q,k,v], bf16/e4m3/e4m3 [k,v], e4m3/e4m3/int8 [q,k,v]; with D=192 the first "
+                "five except bf16/bf16/e4m3 without a V scale",
                 (int)p->q.dtype, (int)p->k.dtype, (int)p->v.dtype, sb[0], sb[1], sb[2]);
   if (empty) return ok();
 

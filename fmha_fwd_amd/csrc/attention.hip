@@ -1,12 +1,13 @@
 // Fused attention forward for gfx950: block-scaled int8 / E4M3 / bf16 Q and
-// K, E4M3 or bf16 V and P, online softmax with lazy rescaling, bf16 output
-// (or E4M3 with a per-head output scale).
+// K, E4M3 or bf16 V and P (or an int8 V with an E4M3 P), online softmax with
+// lazy rescaling, bf16 output (or E4M3 with a per-head output scale).
 //
 // Method sources (FlashInfer pull-request write-ups):
 //  * #2711 page "FlashInfer의 DiT 최적화: SageAttention과 Int8/FP8 혼합 정밀도
 //    커널 도입 분석", 코드 분석 2: per-block Q/K/P/V scale factors that undo
 //    the quantisation after BMM1 (QK^T) and BMM2 (PV); 코드 분석 1: Q, K, V
-//    formats chosen independently.
+//    formats chosen independently; 왜 이게 좋은 최적화인가? 3: K in fp8 with
+//    V in int8 as one such combination.
 //  * #5900 page "Blackwell 아키텍처를 위한 FlashInfer의 FP8/BF16 혼합 정밀도
 //    Attention 최적화 분석", 코드 분석 3: lazy correction (O is rescaled only
 //    when the row maximum grows by 2^8); 코드 분석 1: QK in bf16 or fp8 with an
@@ -36,6 +37,9 @@
 //    product is scaled into O).
 //  * Row sums of an E4M3 P come from one more MFMA (a 0/1 matrix times the P
 //    operand) instead of VALU conversions and additions.
+//  * An int8 V meets the E4M3 P on the fp16 MFMA: no 8-bit product takes an
+//    int8 and an E4M3 operand, and both code sets are fp16 values, so the
+//    widened products are the exact code products.
 //  * sfs_p cancels between numerator and denominator, so it enters only the
 //    quantisation of P (exp2 argument shifted by log2 sfs_p).
 #include <type_traits>
@@ -125,6 +129,9 @@ struct Cfg {
   // E4M3 K under a bf16 Q stays E4M3 in LDS and is widened (exactly) to bf16
   // as each MFMA operand is read.
   static constexpr bool WIDEN = MT == FMT_BF16 && KF == FMT_E4M3;
+  // P in E4M3 (row sums on the matrix core, 8-bit V tiles) for an E4M3 or an
+  // int8 V; an int8 V meets P on the fp16 product (both widen exactly)
+  static constexpr bool P8 = VF != FMT_BF16;
   static constexpr int KROW = KF == FMT_BF16 ? 2 * D : D;        // bytes per K row (HBM and LDS)
   static constexpr int VROW = VF == FMT_BF16 ? 2 * D : D;
   // LDS rows are padded so that every lane reads at a fixed offset from its
@@ -145,6 +152,7 @@ struct Cfg {
   static_assert(K_BUF % 1024 == 0 && V_BUF % 1024 == 0, "DMA granularity");
   static_assert(!(KF == FMT_E4M3 && QF == FMT_INT8), "unsupported");
   static_assert(QF == KF || (QF == FMT_BF16 && KF == FMT_E4M3), "unsupported");
+  static_assert(VF != FMT_INT8 || (QF == FMT_E4M3 && D == 128 && VS_), "int8 V: E4M3 Q and K, head dim 128");
 };
 
 // Q operand registers of one lane (query l % 32, contraction slice of group g).
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   else kb_lane = m32 * C::KP + 16 * g;
   const int tr_G = lane >> 4;
   int vb_lane;
-  if constexpr (C::VF == FMT_E4M3)  // source row 16g + r, column 16(G%2) + 8h
+  if constexpr (C::P8)  // source row 16g + r, column 16(G%2) + 8h
     vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 1)) * C::VP + 16 * (tr_G & 1) + 8 * (lane & 1);
   else  // bf16 V: source row 16g + r, byte column 32(G%2) + 8h'
     vb_lane = (16 * (tr_G >> 1) + ((lane & 15) >> 2)) * C::VP + 32 * (tr_G & 1) + 8 * (lane & 3);
@@ -789,7 +797,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
       const float e_mt = __builtin_amdgcn_exp2f(m_run - tmax);
       const float alpha = trig ? e_mt : 1.0f;
       m_run = trig ? tmax : m_run;
-      if constexpr (C::VF == FMT_E4M3) den_acc[0] *= alpha;
+      if constexpr (C::P8) den_acc[0] *= alpha;
       else den *= alpha;
       st.negm = m_run == -kInf ? -kInf : -(m_run + log2sp);
       if constexpr (C::VS && DIRECT) {
@@ -819,7 +827,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         if constexpr (CLAMP) st.s[e] = fminf(st.s[e], 448.0f);
       }
     } else {
-      if constexpr (C::VF == FMT_E4M3) {
+      if constexpr (C::P8) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           int pk = pack_e4m3<false>(st.s[4 * w], st.s[4 * w + 1], any_vgpr());
@@ -888,6 +896,32 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 #pragma unroll
       for (int d = 0; d < C::ND; ++d) vop[d] = read_vop(vb, d);
       pv_e4m3(pt, vop, direct_tag);
+    } else if constexpr (C::VF == FMT_INT8) {
+      // E4M3 P and int8 V on the 32x32x16 fp16 product: both widen to fp16
+      // exactly and every product is exact, so O sums the same code products
+      // as the 8-bit path would.  MFMA kk takes the eight keys of transposing
+      // read kk (rows 32(kk/2) + 8(kk%2) down) and P bytes 8kk .. 8kk+7.
+      constexpr bool DIRECT = decltype(direct_tag)::value;
+      den_acc = mfma_f8_16(ones_a, pt.pb, den_acc);
+      v8h pf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pf[kk] = e4m3x8_to_f16(pt.pb[2 * kk], pt.pb[2 * kk + 1]);
+#pragma unroll
+      for (int d = 0; d < C::ND; ++d) {
+        v16f acc = (!C::VS || DIRECT) ? o[d] : v16f{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              FMHA_LDS(v2i, vp + (32 * (kk >> 1) + 8 * (kk & 1)) * C::VP + 32 * d));
+          acc = mfma_f16(int8x8_to_f16(r[0], r[1]), pf[kk], acc);
+        }
+        if constexpr (!C::VS || DIRECT) {
+          o[d] = acc;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(acc[r], pt.f, o[d][r]);
+        }
+      }
     } else {
       // bf16 P and V (V unscaled).
 #pragma unroll
@@ -926,7 +960,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;
+    const bool clamp = C::P8 && a.clamp_p;
     auto sub_step = [&](int t, int T, auto u_tag, auto edge_tag, auto clamp_tag, auto direct_tag) {
       constexpr int u = decltype(u_tag)::value;
       const int bv = T & 1;
@@ -1042,7 +1076,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
     while (tc < n_sub) step(std::true_type{}, clamp_tag, direct_tag, BufRt{});
   };
-  const bool clamp = C::VF == FMT_E4M3 && a.clamp_p;
+  const bool clamp = C::P8 && a.clamp_p;
   if constexpr (C::VS) {
     if (clamp) {
       if (v_direct) run(std::true_type{}, std::true_type{});
@@ -1060,7 +1094,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 
   // ---- epilogue: O = num / den in bf16 (or E4M3); rows without a valid key give 0
   float dt;
-  if constexpr (C::VF == FMT_E4M3) dt = den_acc[0];
+  if constexpr (C::P8) dt = den_acc[0];
   else dt = den + __shfl_xor(den, 32, 64);
   const float inv = dt > 0.0f ? sv_ref / dt : 0.0f;
   if (qi >= a.Sq) FMHA_END_TILE;
@@ -1176,6 +1210,7 @@ bool fwd_supported(const FwdKey& k) {
   if (k.qf == FMT_BF16 && k.kf == FMT_BF16 && k.vf == FMT_E4M3) return !k.q_scaled && !k.k_scaled;
   if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return k.q_scaled && k.k_scaled && k.v_scaled;
   if (k.qf == FMT_BF16 && k.kf == FMT_E4M3 && k.vf == FMT_E4M3) return !k.q_scaled && k.k_scaled && k.v_scaled;
+  if (k.qf == FMT_E4M3 && k.kf == FMT_E4M3 && k.vf == FMT_INT8) return k.q_scaled && k.k_scaled && k.v_scaled;
   return false;
 }
 
@@ -1239,6 +1274,8 @@ hipError_t launch_fwd(const FwdKey& k, const FwdArgs& a, hipStream_t s) {
     if (k.v_scaled) return dispatch_layout<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, true>(k, a, s);
     return dispatch_layout<FMT_BF16, FMT_BF16, FMT_E4M3, false, false, false>(k, a, s);
   }
+  if (k.qf == FMT_E4M3 && k.vf == FMT_INT8)
+    return dispatch_layout<FMT_E4M3, FMT_E4M3, FMT_INT8, true, true, true>(k, a, s);
   if (k.qf == FMT_E4M3)
     return dispatch_layout<FMT_E4M3, FMT_E4M3, FMT_E4M3, true, true, true>(k, a, s);
   return dispatch_layout<FMT_BF16, FMT_E4M3, FMT_E4M3, false, true, true>(k, a, s);

@@ -15,6 +15,8 @@ typedef __attribute__((ext_vector_type(2))) float v2f;
 typedef __attribute__((ext_vector_type(4))) float v4f;
 typedef __attribute__((ext_vector_type(16))) float v16f;
 typedef __attribute__((ext_vector_type(8))) __bf16 v8bf;
+typedef __attribute__((ext_vector_type(8))) _Float16 v8h;
+typedef __attribute__((ext_vector_type(2))) _Float16 v2h;
 typedef __attribute__((ext_vector_type(4))) short v4s;
 typedef __attribute__((ext_vector_type(2))) unsigned short v2us;
 
@@ -27,6 +29,9 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;  // byte in LDS
 // result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
@@ -64,6 +69,37 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
   const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// Eight E4M3 codes (byte i of w0:w1 = element i) -> eight fp16, exactly
+// (E4M3's exponents -9 .. 8 and three fraction bits lie inside fp16's).
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// Eight int8 codes (byte i of w0:w1 = element i) -> eight fp16, exactly.
+// With its sign bit flipped a code c reads as the unsigned byte c + 128;
+// placed under the fp16 pattern 0x64 (1024, unit spacing up to 2048) it is
+// the half 1152 + c, and one packed subtraction of 1152 leaves c.
+__device__ __forceinline__ v8h int8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+  // v_perm byte selectors: 0-3 pick bytes of the second source, 4 byte 0 of
+  // the first (0x64)
+  const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                         __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+  const v2h off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  v8h r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2h x = __builtin_bit_cast(v2h, h[i]) - off;
+    r[2 * i] = x[0];
+    r[2 * i + 1] = x[1];
+  }
+  return r;
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);

@@ -72,6 +72,18 @@ class Spec:
     def v_scaled(self):
         return self.v_fmt != "bf16"
 
+    @property
+    def p_fmt(self):
+        """Format P is requantized to before the PV product: bf16 for a bf16
+        V, E4M3 for an E4M3 or an int8 V."""
+        return "bf16" if self.v_fmt == "bf16" else "e4m3"
+
+    @property
+    def pv_mfma(self):
+        """Operand format of the matrix-core PV product: an int8 V meets the
+        E4M3 P in fp16 (both widen exactly), the others use P's format."""
+        return "f16" if self.v_fmt == "int8" else self.p_fmt
+
     def pairs(self):
         """Unmasked (query, key) pairs: the FLOP count is 4 * D * pairs.
         Causal is bottom-right aligned: query i of n_q sees keys <= i + S - n_q."""
@@ -103,6 +115,8 @@ SPECS = {
     "gqa_d192": Spec("gqa_d192", 10, 2, 64, 8, 8192, "e4m3", "e4m3", "e4m3", causal=True, D=192),
     "dit_d192": Spec("dit_d192", 11, 1, 40, 40, 32760, "bf16", "bf16", "e4m3", D=192),
     "sparse_d192": Spec("sparse_d192", 12, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True, paged=True, D=192),
+    # the gqa shape with K in E4M3 and V in int8 (per-64-token scales, amax/127)
+    "gqa_vi8": Spec("gqa_vi8", 13, 2, 64, 8, 8192, "e4m3", "e4m3", "int8", causal=True),
     # the sparse inputs (same spawn key: same Q, K, V and mask) with K/V contiguous instead of paged
     "sparse_contig": Spec("sparse_contig", 4, 4, 32, 32, 16384, "bf16", "e4m3", "e4m3", masked=True),
     # ... and with no block mask at all: the dense attention the mask thins out

@@ -157,7 +157,8 @@ typedef struct {
   /* Per-block scale factors, fp32 [B, H, ceil(S / 64)] contiguous (H = Hq for
    * sfs_q, Hkv for sfs_k / sfs_v; S = Sq or Skv, counted in logical tokens),
    * or NULL for an unscaled operand.  An int8 / E4M3 Q or K needs its scale
-   * (sage_block = 64); V may be E4M3 with (64) or without (0) a scale. */
+   * (sage_block = 64); V may be E4M3 with (64) or without (0) a scale, and
+   * an int8 V needs its scale. */
   const float* sfs_q;
   const float* sfs_k;
   const float* sfs_v;
@@ -203,8 +204,9 @@ typedef struct {
  * ascending 64-key sub-tiles; the reference maximum m moves to a sub-tile's
  * maximum t only when m is unset or t - m > tau, and only then are the
  * running numerator and denominator multiplied by 2^(m - t).
- *   P = 2^(s2 - m);  w = Qp(P / sp) * sp  (Qp = E4M3 for an E4M3 V, bf16
- *   for a bf16 V; sp = sfs_p[h] or 1);  num += w V[j] * sfs_v;  den += w.
+ *   P = 2^(s2 - m);  w = Qp(P / sp) * sp  (Qp = E4M3 for an E4M3 or an
+ *   int8 V, bf16 for a bf16 V; sp = sfs_p[h] or 1);  num += w V[j] * sfs_v;
+ *   den += w.
  *   o[i] = bf16(num / den), or 0 for a row without a valid key; an E4M3 o
  *   holds encode(num / den / so) instead (so = sfs_o[h] or 1).
  *
@@ -214,6 +216,11 @@ typedef struct {
  *   (bf16, bf16, e4m3)          [v] or none
  *   (e4m3, e4m3, e4m3)          [q, k, v]
  *   (bf16, e4m3, e4m3)          [k, v]
+ *   (e4m3, e4m3, int8)          [q, k, v], head dim 128: the #2711 page's
+ *                               K-fp8 / V-int8 example of separate K and V
+ *                               types (왜 이게 좋은 최적화인가? 3); V codes
+ *                               are amax/127 block codes as fmha_quantize_blocks
+ *                               writes them
  * o is bf16 or E4M3 for each of them.  Other combinations return
  * FMHA_ERR_UNSUPPORTED.
  */

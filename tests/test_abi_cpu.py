@@ -89,7 +89,7 @@ def _call(lib, p):
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(D=64), F.FMHA_ERR_UNSUPPORTED, "D=64"),
     (dict(D=192, sfs_v=None, sage_block_v=0), F.FMHA_ERR_UNSUPPORTED,
-     "with D=192 the same except"),                                # bf16/bf16/e4m3 without V scale at 192
+     "with D=192 the first five except"),                          # bf16/bf16/e4m3 without V scale at 192
     (dict(D=192, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), sfs_k=FAKE, sage_block_k=64,
           block_mask=FAKE, mask_block_q=64, mask_block_kv=256), F.FMHA_ERR_UNSUPPORTED, "no kernel"),  # unscaled E4M3 Q
     (dict(Hq=6, Hkv=4), F.FMHA_ERR_INVALID, "multiple"),
@@ -108,7 +108,12 @@ def _call(lib, p):
     (dict(o=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "bf16 or e4m3"),
     (dict(sfs_o=FAKE), F.FMHA_ERR_INVALID, "sfs_o given"),
     (dict(o=_tensor(F.FMHA_DT_E4M3), sfs_o=FAKE + 2), F.FMHA_ERR_INVALID, "sfs_o misaligned"),
-    (dict(v=_tensor(F.FMHA_DT_INT8)), F.FMHA_ERR_UNSUPPORTED, "int8 V"),
+    (dict(v=_tensor(F.FMHA_DT_INT8, ss=128)), F.FMHA_ERR_UNSUPPORTED, "no kernel"),            # int8 V, bf16 Q/K
+    (dict(D=192, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), v=_tensor(F.FMHA_DT_INT8, ss=192),
+          sfs_q=FAKE, sage_block_q=64, sfs_k=FAKE, sage_block_k=64), F.FMHA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), v=_tensor(F.FMHA_DT_INT8, ss=128),
+          sfs_q=FAKE, sage_block_q=64, sfs_k=FAKE, sage_block_k=64, sfs_v=None, sage_block_v=0),
+     F.FMHA_ERR_UNSUPPORTED, "no kernel"),                                                     # unscaled int8 V
     (dict(q=_tensor(7)), F.FMHA_ERR_INVALID, "dtype"),
     (dict(sage_block_v=32), F.FMHA_ERR_UNSUPPORTED, "sage_block_v"),
     (dict(sage_block_v=0), F.FMHA_ERR_INVALID, "sfs_v given"),
@@ -154,6 +159,15 @@ def test_fwd_null_params(lib):
 
 def test_fwd_empty_problem_is_a_no_op(lib):
     rc, err = _call(lib, _params(Sq=0))
+    assert rc == F.FMHA_OK and err == ""
+
+
+def test_fwd_accepts_e4m3_k_with_int8_v(lib):
+    # the K-fp8 / V-int8 combination passes validation (an empty problem, so
+    # nothing is launched)
+    p = _params(Sq=0, q=_tensor(F.FMHA_DT_E4M3), k=_tensor(F.FMHA_DT_E4M3), v=_tensor(F.FMHA_DT_INT8, ss=128),
+                sfs_q=FAKE, sage_block_q=64, sfs_k=FAKE, sage_block_k=64)
+    rc, err = _call(lib, p)
     assert rc == F.FMHA_OK and err == ""
 
 

@@ -36,14 +36,14 @@ def _run_small(spec, **kw):
 
 
 @pytest.mark.parametrize("S", [1, 63, 64, 65, 255, 320])
-@pytest.mark.parametrize("base", ["tiny", "dit_i8", "dit", "gqa"])
+@pytest.mark.parametrize("base", ["tiny", "dit_i8", "dit", "gqa", "gqa_vi8"])
 def test_small_dense(base, S):
-    B, Hq, Hkv = {"tiny": (1, 2, 2), "dit_i8": (1, 3, 3), "dit": (2, 2, 2), "gqa": (2, 8, 2)}[base]
+    B, Hq, Hkv = {"tiny": (1, 2, 2), "dit_i8": (1, 3, 3), "dit": (2, 2, 2), "gqa": (2, 8, 2), "gqa_vi8": (2, 8, 2)}[base]
     _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv))
 
 
 @pytest.mark.parametrize("S", [1, 65, 200, 320])
-@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8"])
+@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8", "gqa_vi8"])
 def test_small_causal(base, S):
     _run_small(W.small_spec(base, S, B=1, Hq=4, Hkv=2, causal=True))
 
@@ -59,10 +59,10 @@ def test_small_sparse_contiguous(S):
     _run_small(W.small_spec("sparse", S, B=1, Hq=2, Hkv=2, paged=False))
 
 
-@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8", "gqa"])
+@pytest.mark.parametrize("base", ["tiny", "dit", "dit_i8", "gqa", "gqa_vi8"])
 @pytest.mark.parametrize("masked,paged", [(True, False), (False, True), (True, True)])
 def test_other_formats_masked_or_paged(base, masked, paged):
-    # the block-sparse and paged paths for the other four format combinations
+    # the block-sparse and paged paths for the other format combinations
     _run_small(W.small_spec(base, 300, B=2, Hq=4, Hkv=2, masked=masked, paged=paged))
 
 
@@ -77,7 +77,7 @@ def test_small_paged_page_sizes(page_size, masked):
     _run_small(W.small_spec("sparse", 300, B=2, Hq=2, Hkv=2, masked=masked, page_size=page_size))
 
 
-@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "sparse", "tiny"])
+@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "sparse", "tiny", "gqa_vi8"])
 def test_sfs_p_and_tau_variants(base):
     spec = W.small_spec(base, 320, B=1, Hq=4, Hkv=2)
     sp = torch.tensor([1.0, 0.25, 0.1, 2.0], dtype=torch.float32, device="cuda")
@@ -87,7 +87,7 @@ def test_sfs_p_and_tau_variants(base):
 
 
 @pytest.mark.parametrize("base,D", [("tiny", 128), ("dit", 128), ("dit_i8", 128), ("gqa", 128), ("sparse", 128),
-                                    ("gqa", 192), ("dit", 192)])
+                                    ("gqa_vi8", 128), ("gqa", 192), ("dit", 192)])
 @pytest.mark.parametrize("scale", [0.01, 0.3])
 def test_softmax_scale_variants(base, D, scale):
     # a flatter (0.01) and a sharper (0.3) softmax than 1/sqrt(D): the
@@ -195,7 +195,7 @@ def test_kv_sequence_beyond_2gib():
 @pytest.mark.parametrize("base,S,causal,D", [("tiny", 200, False, 128), ("dit", 320, False, 128),
                                              ("dit_i8", 300, False, 128), ("gqa", 300, True, 128),
                                              ("sparse", 300, False, 128), ("dit", 320, False, 192),
-                                             ("gqa", 300, True, 192)])
+                                             ("gqa", 300, True, 192), ("gqa_vi8", 300, True, 128)])
 def test_e4m3_output(base, S, causal, D):
     # O / sfs_o encoded to E4M3 in the epilogue; the per-head scales spread
     # the outputs over the E4M3 range (saturation and subnormals included).
@@ -230,7 +230,7 @@ def test_e4m3_output(base, S, causal, D):
     print(f"e4m3 output {spec.name}: {n_diff} of {codes.size} codes differ from the oracle's encoding")
 
 
-@pytest.mark.parametrize("base,skv", [("dit", 100), ("gqa", 70), ("dit_i8", 1)])
+@pytest.mark.parametrize("base,skv", [("dit", 100), ("gqa", 70), ("dit_i8", 1), ("gqa_vi8", 130)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_more_queries_than_keys(base, skv, causal):
     # Sq = 300 queries against fewer keys; bottom-right causal leaves the
@@ -345,7 +345,7 @@ def test_query_chunk_gqa(sq, S, causal):
     _run_small(W.small_spec("gqa", S, B=1, Hq=8, Hkv=2, causal=causal, sq=sq))
 
 
-@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "tiny", "sparse"])
+@pytest.mark.parametrize("base", ["gqa", "dit", "dit_i8", "tiny", "sparse", "gqa_vi8"])
 @pytest.mark.parametrize("hq,sq", [(16, 1), (16, 5), (16, 16), (32, 3), (32, 8), (64, 1), (64, 4)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rows_of_several_heads_per_wave(base, hq, sq, causal):
@@ -362,13 +362,20 @@ def test_short_query_ranges_at_head_dim_192(base, hq, sq):
     _run_small(W.small_spec(base, 300, B=2, Hq=hq, Hkv=2, causal=True, sq=sq, masked=False, D=192))
 
 
-@pytest.mark.parametrize("base", ["gqa", "dit_i8", "sparse"])
+@pytest.mark.parametrize("base", ["gqa", "dit_i8", "sparse", "gqa_vi8"])
 @pytest.mark.parametrize("sq", [1, 7, 16])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rows_of_two_heads_in_two_wave_workgroups(base, sq, causal):
     # four query heads per KV head: two-wave workgroups of two heads per wave
     # (8-bit K formats)
     _run_small(W.small_spec(base, 300, B=2, Hq=8, Hkv=2, causal=causal, sq=sq, masked=False))
+
+
+@pytest.mark.parametrize("sq,S", [(1, 300), (40, 511), (96, 700)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_query_chunk_int8_v(sq, S, causal):
+    # the K-fp8 / V-int8 combination on a prefill chunk of a GQA group
+    _run_small(W.small_spec("gqa_vi8", S, B=1, Hq=8, Hkv=2, causal=causal, sq=sq))
 
 
 @pytest.mark.parametrize("S", [1, 130, 320])
@@ -392,7 +399,7 @@ def test_head_dim_192(base, B, Hq, Hkv, causal, sq, S):
     _run_small(W.small_spec(base, S, B=B, Hq=Hq, Hkv=Hkv, causal=causal, sq=sq, D=192))
 
 
-@pytest.mark.parametrize("base", ["dit", "gqa", "dit_i8", "sparse"])
+@pytest.mark.parametrize("base", ["dit", "gqa", "dit_i8", "sparse", "gqa_vi8"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_v_block_scales_spanning_more_than_2_64(base, causal):
     # V block scales more than 2^64 apart: the kernel then keeps O in fixed
@@ -474,6 +481,7 @@ FULL = [
     ("sparse_d192", [(0, 0), (3, 31)], "sample"),
     ("sparse_contig", [(1, 5), (2, 17)], "sample"),
     ("sparse_dense", [(0, 3), (3, 30)], "sample"),
+    ("gqa_vi8", [(0, 0), (1, 63)], "sample"),
 ]
 
 
