@@ -73,6 +73,13 @@ constexpr int kDenseWaves = FMHA_DENSE_WAVES;  // wavefronts (x 32 queries) per 
 #ifndef FMHA_HEAD_PACK
 #define FMHA_HEAD_PACK 1  // 0: never pack query heads into one workgroup
 #endif
+// 1: the per-row O factor of the fast V-reference path is applied to one
+// d-tile right before that d-tile's PV product is issued, so the multiplies
+// of the next d-tile run while the matrix core works on the previous one
+// (0: all of O is rescaled in the softmax, before the first PV product).
+#ifndef FMHA_PV_INTERLEAVE
+#define FMHA_PV_INTERLEAVE 1
+#endif
 constexpr float kInf = __builtin_huge_valf();
 
 // Key held by row m of a 32-key MFMA tile: lane group g of the S^T result
@@ -749,7 +756,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 
   // Softmax of one sub-tile, written as eight stages of separable work:
   //   0: row max, lazy decision, rescale of den (and of O off the fast path);
-  //   1-2: rescale of O, half the d-tiles each (fast V-reference path);
+  //   1-2: rescale of O, half the d-tiles each (fast V-reference path, E4M3
+  //        V excepted: there the PV step rescales each d-tile just before
+  //        its product);
   //   3-6: P = 2^(s2 - m) / sp for eight keys each, clamped to the E4M3 range
   //        only where P / sp can reach it (sfs_p given or tau above log2 448);
   //   7: P to the PV operand format (bf16 P: also den += P).
@@ -764,6 +773,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     constexpr bool EDGE = decltype(edge_tag)::value;
     constexpr bool CLAMP = decltype(clamp_tag)::value;
     constexpr bool DIRECT = decltype(direct_tag)::value;
+    constexpr bool INTERLEAVE = FMHA_PV_INTERLEAVE && C::VF == FMT_E4M3;
     if constexpr (K == 0) {
       st.pt.f = 1.0f;
 #pragma unroll
@@ -804,6 +814,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         // one factor folds the lazy rescale and the change of V reference
         st.fo = alpha * (sv_ref * __builtin_amdgcn_rcpf(sv_t));
         sv_ref = sv_t;
+        if constexpr (INTERLEAVE) st.pt.f = st.fo;  // applied by the PV step
       } else {
         if (__ballot(trig) != 0) {
 #pragma unroll
@@ -814,7 +825,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
         if constexpr (C::VS) st.pt.f = sv_t / sv_ref;  // reference stays at 1
       }
     } else if constexpr (K == 1 || K == 2) {
-      if constexpr (C::VS && DIRECT) {
+      if constexpr (C::VS && DIRECT && !INTERLEAVE) {
 #pragma unroll
         for (int d = (C::ND / 2) * (K - 1); d < (K == 2 ? C::ND : C::ND / 2); ++d)
 #pragma unroll
@@ -880,7 +891,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     den_acc = mfma_f8_16(ones_a, pt.pb, den_acc);
 #pragma unroll
     for (int d = 0; d < C::ND; ++d) {
-      if constexpr (!C::VS || DIRECT) {
+      if constexpr (C::VS && DIRECT && FMHA_PV_INTERLEAVE) {
+        // O factor of this d-tile, then its product; the next d-tile's
+        // multiplies are ordered after this product's issue
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= pt.f;
+        o[d] = mfma_f8(vop[d], pt.pb, o[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (!C::VS || DIRECT) {
         o[d] = mfma_f8(vop[d], pt.pb, o[d]);
       } else {
         const v16f part = mfma_f8(vop[d], pt.pb, v16f{});
