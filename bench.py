@@ -67,6 +67,26 @@ def pair_count(spec, data):
     return spec.pairs()
 
 
+ESIZE = {"bf16": 2, "e4m3": 1, "int8": 1}
+
+
+def attention_bytes(spec):
+    """Algorithmic HBM bytes of one fmha_fwd launch: every operand byte read
+    once (Q, K, V, their 64-token block scales, the block mask and the page
+    table where used) and the bf16 output written once."""
+    B, Hq, Hkv, S, D, nq = spec.B, spec.Hq, spec.Hkv, spec.S, spec.D, spec.n_q
+    nb = lambda n: -(-n // 64)  # noqa: E731
+    b = B * Hq * nq * D * ESIZE[spec.q_fmt] + B * Hkv * S * D * (ESIZE[spec.k_fmt] + ESIZE[spec.v_fmt])
+    b += B * Hq * nq * D * 2
+    b += 4 * ((B * Hq * nb(nq) if spec.q_fmt != "bf16" else 0) + (B * Hkv * nb(S) if spec.k_fmt != "bf16" else 0)
+              + (B * Hkv * nb(S) if spec.v_fmt != "bf16" else 0))
+    if spec.masked:
+        b += B * Hq * nb(nq) * -(-S // 256)
+    if spec.paged:
+        b += B * -(-S // spec.page_size) * 4
+    return b
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -463,6 +483,13 @@ def main():
         sclk_live = None
     sclk = sclk_live["ghz_median"] if sclk_live else sclk_counters
 
+    # The binding roofline of the launch: matrix-core time of its FLOPs at the
+    # dtype peak against HBM time of its algorithmic bytes at the HBM peak
+    # (short query ranges over a long K/V cache are HBM-bound).
+    abytes = attention_bytes(spec)
+    hbm_bound = abytes / (HBM_PEAK_GBS * 1e9) > flops / (peak * 1e12)
+    gbs = abytes / (fwd_ms * 1e-3) / 1e9
+    frac = gbs / HBM_PEAK_GBS if hbm_bound else achieved / peak
     rec = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -480,15 +507,19 @@ def main():
                    "d": spec.D, "q": spec.q_fmt, "k": spec.k_fmt, "v": spec.v_fmt, "p": spec.p_fmt,
                    "causal": spec.causal, "block_sparse": spec.masked, "paged": spec.paged,
                    "unmasked_pairs": pairs, "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "fmha_fwd", "frac_of_fp8_peak": achieved / PEAK["e4m3"],
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": gbs if hbm_bound else achieved,
+                     "peak": HBM_PEAK_GBS if hbm_bound else peak, "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                     "frac": frac, "traffic": traffic,
+                     "kernel": "fmha_fwd", "algorithmic_bytes": abytes,
+                     "mfma_tflops": achieved, "mfma_peak": peak, "mfma_frac": achieved / peak,
+                     "frac_of_fp8_peak": achieved / PEAK["e4m3"],
                      # shader clock while the timed steps ran (sysfs, median of the samples; else
                      # the counter record's), and the fraction of the peak at that clock (the
                      # published peaks assume 2.4 GHz)
                      "sclk_ghz_measured": sclk,
                      "sclk_sysfs": sclk_live, "sclk_ghz_counters": sclk_counters,
-                     "frac_at_measured_sclk": None if sclk is None else achieved / (peak * min(sclk, 2.4) / 2.4)},
+                     "frac_at_measured_sclk": None if sclk is None or hbm_bound
+                     else achieved / (peak * min(sclk, 2.4) / 2.4)},
         "fwd_ms": fwd_ms,
         "fwd_ms_median": fwd_median,
         "fwd_ms_min": fwd_min,

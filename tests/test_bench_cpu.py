@@ -58,3 +58,19 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_attention_bytes_closed_forms():
+    # DiT-scale launch: bf16 Q, K and output, E4M3 V with one fp32 scale per 64 tokens
+    dit = W.SPECS["dit"]
+    n = 40 * 32760 * 128
+    assert bench.attention_bytes(dit) == n * 2 + n * 2 + n * 1 + n * 2 + 40 * 512 * 4
+    # 16 new positions of 64 sequences over an 8192-token E4M3 cache with 8 KV heads
+    step = W.SPECS["gqa4_step"]
+    q = 64 * 32 * 16 * 128
+    kv = 64 * 8 * 8192 * 128
+    scales = 4 * (64 * 32 * 1 + 2 * 64 * 8 * 128)
+    assert bench.attention_bytes(step) == q + 2 * kv + 2 * q + scales
+    # its bytes take longer at the HBM peak than its FLOPs at the fp8 peak; dit's the other way round
+    assert step.pairs() * 4 * 128 / 5000e12 < bench.attention_bytes(step) / 8000e9
+    assert dit.pairs() * 4 * 128 / bench.mixed_peak("bf16", "e4m3") / 1e12 > bench.attention_bytes(dit) / 8000e9
